@@ -1,0 +1,147 @@
+"""Pins for oracle/gemm.py and oracle/static_fp8.py: brute-force loops on tiny
+shapes, special cases, the sqnr closed forms and calibration properties."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import codecs as C
+from oracle import gemm as G
+from oracle import quant as Q
+from oracle import static_fp8 as S
+from weight_only_bit_dequant_amd import synth
+
+
+def _bf(x):
+    return C.f32_to_bf16(np.asarray(x, np.float32))
+
+
+def _loop_linear(Xb, Wd, bb):
+    """Triple loop with exact rational-free fsum: y[m][n] = sum_k x[m][k] w[n][k] + b[n]."""
+    x = C.bf16_to_f32(Xb).astype(float)
+    M, K = x.shape
+    N = Wd.shape[0]
+    b = C.bf16_to_f32(bb).astype(float) if bb is not None else np.zeros(N)
+    y = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            y[m, n] = math.fsum([x[m, k] * Wd[n, k] for k in range(K)] + [b[n]])
+    return y
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp8", "nvfp4", "mxfp4"])
+def test_linear_fp64_vs_triple_loop(fmt):
+    # non-square on purpose (a transposed operand cannot fit), small enough to loop
+    N, K, M = 32, 256, 3
+    W, b, X = synth.linear_case(N, K, M, cfg=40)
+    codes, s, g = Q.quantize(fmt, W)
+    Wd = Q.dequant(fmt, codes, s, g)
+    y = G.linear_fp64(X, Wd, b)
+    ref = _loop_linear(X, Wd, b)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # dequantized weight equals code-times-scale written independently
+    if fmt == "int4":
+        cs = np.array([[int(c) for c in row] for row in codes], float)
+        sc = C.bf16_to_f32(s).astype(float)
+        indep = cs * np.repeat(sc, 128, axis=1)
+        assert np.array_equal(Wd, indep)
+
+
+def test_linear_special_cases():
+    N, K, M = 32, 128, 2
+    W, b, X = synth.linear_case(N, K, M, cfg=41)
+    # all-zero weight -> Y = b
+    y = G.linear_fp64(X, np.zeros((N, K)), b)
+    assert np.array_equal(y, np.broadcast_to(C.bf16_to_f32(b).astype(float), (M, N)))
+    # one-hot weight selects one X column (and exercises W's orientation)
+    Wd = np.zeros((N, K))
+    Wd[5, 17] = 1.0
+    y = G.linear_fp64(X, Wd, None)
+    x = C.bf16_to_f32(X).astype(float)
+    assert np.array_equal(y[:, 5], x[:, 17])
+    assert not y[:, np.arange(N) != 5].any()
+    with pytest.raises(ValueError):
+        G.linear_fp64(X, np.zeros((N, K + 1)), None)
+
+
+def test_sqnr_closed_forms():
+    rng = np.random.default_rng(4)
+    a = rng.standard_normal(1000).astype(np.float32)
+    assert G.sqnr(a, np.zeros_like(a)) == pytest.approx(0.0, abs=1e-5)
+    eps = 1e-3
+    assert G.sqnr(a, a * (1 + eps)) == pytest.approx(-20 * math.log10(eps), abs=1e-3)
+    a64 = a.astype(np.float64)
+    assert G.sqnr_fp64(a64, a64 * (1 + eps)) == pytest.approx(60.0, abs=1e-9)
+    na = float(np.linalg.norm(a.astype(np.float64)))
+    assert G.sqnr(a, a) == pytest.approx(20 * math.log10(na / 1e-12), abs=1e-3)
+    # rel-Frobenius 1e-2 <-> 40 dB
+    assert G.rel_frobenius(a64 * 1.01, a64) == pytest.approx(0.01, rel=1e-12)
+    assert G.sqnr_fp64(a64, a64 * 1.01) == pytest.approx(40.0, abs=1e-9)
+
+
+# ------------------------------------------------------------------ static FP8
+
+
+def test_quantize_act_bruteforce():
+    X = synth.activations(4, 64, 50)
+    amax = S.absmax(X)
+    s = S.scale_from_amax(amax)
+    assert s == np.float32(np.float32(amax) / np.float32(448))
+    codes = S.quantize_act(X, s)
+    q = (C.bf16_to_f32(X) / s).astype(np.float32).astype(np.float64)
+    vals = C.e4m3_decode(np.arange(0x7F))
+    mag = np.argmin(np.abs(np.abs(q)[..., None] - vals) + (np.arange(0x7F) % 2) * 1e-12, axis=-1)
+    assert np.array_equal(codes, (mag | (np.signbit(q) << 7)).astype(np.uint8))
+    # the absmax element maps to +-448
+    i = np.unravel_index(np.abs(C.bf16_to_f32(X)).argmax(), X.shape)
+    assert codes[i] in (0x7E, 0xFE)
+
+
+def test_static_linear_vs_loop():
+    N, K, M = 16, 64, 3
+    W = synth.linear_weight(N, K, 51)
+    X = synth.activations(M, K, 52)
+    wq, ws = Q.quantize_fp8_row(W)
+    s = S.scale_from_amax(S.absmax(X))
+    xq = S.quantize_act(X, s)
+    y = S.static_linear_fp64(xq, s, wq, ws)
+    xd = C.e4m3_decode(xq)
+    wd = C.e4m3_decode(wq)
+    ref = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            ref[m, n] = math.fsum(xd[m, k] * wd[n, k] for k in range(K)) * float(s) * float(ws[n])
+    assert np.allclose(y, ref, rtol=1e-12, atol=0)
+
+
+def test_calibration_properties():
+    weights = synth.mlp_weights()
+    batches = synth.calibration_batches(32, 256)
+    scales, amax = S.calibrate(batches, weights)
+    # layer-1 amax is the max over the raw batches
+    assert amax[0] == max(np.abs(C.bf16_to_f32(b)).max() for b in batches)
+    # layer-2 amax is over the float model's bf16 layer-1 outputs
+    h = [G.to_bf16(C.bf16_to_f32(b).astype(float) @ C.bf16_to_f32(weights[0]).astype(float).T) for b in batches]
+    assert amax[1] == max(np.abs(C.bf16_to_f32(x)).max() for x in h)
+    assert all(sc == np.float32(a / np.float32(448)) for sc, a in zip(scales, amax))
+    # more calibration data never lowers a scale; the same data gives the same scales
+    scales2, _ = S.calibrate(batches[:3], weights)
+    assert all(a >= b for a, b in zip(scales, scales2))
+    assert S.calibrate(batches, weights)[0] == scales
+
+
+def test_static_two_layer_sqnr_recorded():
+    """End-to-end eager SQNR of the static-FP8 model vs the float model.  The
+    page prints no value ("parity unpinned"); this checks only that the
+    quantized model tracks the float one (FP8 e4m3 keeps ~4 significant bits,
+    so a two-layer model lands far above 20 dB and below the bf16 level)."""
+    weights = synth.mlp_weights()
+    batches = synth.calibration_batches(32, 256)
+    scales, _ = S.calibrate(batches, weights)
+    qw = S.quantize_model(weights)
+    x = synth.activations(32, 256, synth.SEED_X + 5)
+    _, fp_out = S.float_forward(x, weights)
+    _, outs = S.quant_forward(x, scales, qw)
+    v = G.sqnr(C.bf16_to_f32(fp_out), C.bf16_to_f32(outs[-1]))
+    assert 20.0 < v < 40.0

@@ -1,0 +1,231 @@
+"""Pins for oracle/quant.py: hand-worked examples, brute-force code choice,
+invariants the formats force, and packing bytes (no GPU)."""
+
+import numpy as np
+import pytest
+
+from oracle import codecs as C
+from oracle import quant as Q
+from weight_only_bit_dequant_amd import synth
+
+
+def bf16(vals):
+    return C.f32_to_bf16(np.asarray(vals, np.float32))
+
+
+def row_with(vals, K):
+    w = np.zeros(K, np.float32)
+    w[: len(vals)] = vals
+    return w
+
+
+# ------------------------------------------------------------------ INT4
+
+
+def test_int4_hand_example():
+    # group 0: amax 0.875 -> s = 0.875/7 = 0.125 exactly.  Ties go to even:
+    # 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -3.5 -> -4, 6.5 -> 6.
+    g0 = row_with([0.875, -0.875, 0.0625, 0.1875, 0.3125, -0.4375, 0.8125], 128)
+    # group 1: amax 0.99609375 (bf16 0x3F7F); 0.99609375/7 = 0.1422991..
+    # rounds UP to bf16 0.142578125 (0x3E12).  0.498046875 is exactly 3.5
+    # unrounded scales but 3.4931 rounded scales -> code 3 (dividing by the
+    # unrounded scale would give 4).
+    g1 = row_with([0.99609375, -0.99609375, 0.498046875], 128)
+    W = bf16(np.concatenate([g0, g1])[None, :])
+    codes, s = Q.quantize_int4_sym(W, 128)
+    assert s.tolist() == [[0x3E00, 0x3E12]]
+    assert codes[0, :7].tolist() == [7, -7, 0, 2, 2, -4, 6]
+    assert codes[0, 128:131].tolist() == [7, -7, 3]
+    assert not codes[0, 7:128].any() and not codes[0, 131:].any()
+
+
+def _int4_bruteforce(q):
+    """argmin over c in [-8, 7] of |q - c|, ties to the even c."""
+    cands = np.arange(-8, 8)
+    d = np.abs(q[..., None] - cands)
+    key = d * 2 + (cands % 2) * 1e-9  # even wins ties
+    return cands[np.argmin(key, axis=-1)]
+
+
+def test_int4_bruteforce_and_invariants():
+    W = synth.linear_weight(64, 512, 7)
+    codes, s_bits = Q.quantize_int4_sym(W)
+    w = C.bf16_to_f32(W).reshape(64, 4, 128)
+    s = C.bf16_to_f32(s_bits)
+    q = (w / s[..., None]).astype(np.float32)
+    assert np.array_equal(codes.reshape(64, 4, 128), _int4_bruteforce(q.astype(np.float64)))
+    # symmetric: every group reaches +-7 and never -8
+    assert np.all(np.abs(codes.reshape(64, 4, 128)).max(axis=2) == 7)
+    assert codes.min() >= -7
+    # reconstruction within half a step
+    deq = Q.dequant_int4(codes, s_bits)
+    step = np.repeat(s.astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(deq - w.reshape(64, 512)) <= step / 2 * (1 + 1e-6))
+
+
+def test_int4_weight_sqnr_closed_form():
+    # U(-b, b) with per-group scale ~ b/7: SQNR ~ 10 log10(4 * 49) = 22.9 dB
+    # (slightly higher since the group amax sits a little below b)
+    W = synth.linear_weight(256, 1024, 8)
+    codes, s = Q.quantize_int4_sym(W)
+    w = C.bf16_to_f32(W).astype(np.float64)
+    from oracle.gemm import sqnr_fp64
+
+    v = sqnr_fp64(w, Q.dequant_int4(codes, s))
+    assert 22.5 < v < 24.0
+
+
+def test_int4_zero_group_and_shape_check():
+    W = np.zeros((2, 256), np.uint16)
+    codes, s = Q.quantize_int4_sym(W)
+    assert not codes.any() and not s.any()
+    with pytest.raises(ValueError):
+        Q.quantize_int4_sym(np.zeros((2, 100), np.uint16))
+
+
+# ------------------------------------------------------------------ FP8 row
+
+
+def test_fp8_row_hand_example():
+    # amax 0.875 -> s = 0.875/448 = 2^-9 exactly; w/s: 448 -> 0x7E, 32 -> 0x60,
+    # 35 -> 36 (0x61, spacing 4 in [32, 64)), 34 -> tie -> 32 (even, 0x60)
+    w = row_with([0.875, 0.0625, 0.068359375, 0.06640625, -0.875], 16)
+    codes, s = Q.quantize_fp8_row(bf16(w[None, :]))
+    assert s[0] == np.float32(2.0 ** -9)
+    assert codes[0, :5].tolist() == [0x7E, 0x60, 0x61, 0x60, 0xFE]
+
+
+def test_fp8_row_invariants_and_bruteforce():
+    W = synth.linear_weight(128, 384, 9)
+    codes, s = Q.quantize_fp8_row(W)
+    w = C.bf16_to_f32(W)
+    # the row absmax element lands on +-448
+    idx = np.abs(w).argmax(axis=1)
+    top = codes[np.arange(128), idx]
+    assert np.all((top == 0x7E) | (top == 0xFE))
+    # brute force: nearest finite E4M3 value to fp32(w/s), ties to even code
+    q = (w / s[:, None]).astype(np.float32).astype(np.float64)
+    vals = C.e4m3_decode(np.arange(0x7F))
+    a = np.abs(q)[..., None]
+    d = np.abs(a - vals)
+    key = d + (np.arange(0x7F) % 2) * 1e-12
+    mag = np.argmin(key, axis=-1)
+    want = mag | (np.signbit(q) << 7)
+    assert np.array_equal(codes, want.astype(np.uint8))
+
+
+# ------------------------------------------------------------------ NVFP4
+
+
+def test_nvfp4_hand_example():
+    # A = 2.625 = 2688 * 2^-10, so g = 2^-10 exactly.
+    # block 0 (amax 2.625): t = (2.625/6)/2^-10 = 448 -> sc 0x7E, S = 0.4375;
+    #   2.625 -> 6 (0x7), 1.3125 -> 3 (0x5), -0.875 -> -2 (0xC),
+    #   0.21875 -> 0.5 (0x1), 0.109375 -> 0.25 -> tie -> 0 (0x0)
+    # block 1 (amax 0.375): t = 64 -> sc 0x68 (2^6), S = 0.0625;
+    #   0.375 -> 6 (0x7), 0.1875 -> 3 (0x5), -0.03125 -> -0.5 (0x9)
+    b0 = row_with([2.625, 1.3125, -0.875, 0.21875, 0.109375], 16)
+    b1 = row_with([0.375, 0.1875, -0.03125], 16)
+    W = np.zeros((16, 32), np.float32)
+    W[0] = np.concatenate([b0, b1])
+    codes, sc, g = Q.quantize_nvfp4(bf16(W))
+    assert g == np.float32(2.0 ** -10)
+    assert sc[0].tolist() == [0x7E, 0x68]
+    assert codes[0, :5].tolist() == [0x7, 0x5, 0xC, 0x1, 0x0]
+    assert codes[0, 16:19].tolist() == [0x7, 0x5, 0x9]
+    # all-zero blocks clamp their scale to the smallest subnormal (code 0x01)
+    assert np.all(sc[1:] == 0x01) and not codes[1:].any()
+
+
+def test_nvfp4_invariants():
+    W = synth.linear_weight(64, 256, 10)
+    codes, sc, g = Q.quantize_nvfp4(W)
+    w = C.bf16_to_f32(W)
+    A = np.abs(w).max()
+    assert g == np.float32(np.float32(A) / np.float32(2688.0))
+    r, k = np.unravel_index(np.abs(w).argmax(), w.shape)
+    assert sc[r, k // 16] == 0x7E
+    assert codes[r, k] in (0x7, 0xF)
+    S = C.e4m3_decode(sc) * float(g)
+    assert np.all(S > 0)
+    # each block's largest |code value| is 6 or close below it (>= 4)
+    mags = np.abs(C.e2m1_decode(codes)).reshape(64, 16, 16).max(axis=2)
+    assert np.all(mags >= 4)
+    # round trip error within half the E2M1 spacing at 6 (1.0) times S
+    deq = Q.dequant_nvfp4(codes, sc, g)
+    assert np.all(np.abs(deq - w) <= np.repeat(S, 16, axis=1) * 1.0 + 1e-12)
+
+
+def test_nvfp4_shape_rule():
+    with pytest.raises(ValueError):
+        Q.quantize_nvfp4(np.zeros((16, 40), np.uint16))
+    with pytest.raises(ValueError):
+        Q.quantize_nvfp4(np.zeros((24, 32), np.uint16))
+
+
+# ------------------------------------------------------------------ MXFP4
+
+
+def test_mxfp4_hand_example():
+    # block 0 amax 6.0: frexp(6) = (0.75, 3) -> e = 0 (code 127); 5.0 -> tie
+    #   between 4 and 6 -> 4 (0x6); -1.5 -> 0xB
+    # block 1 amax 7.5: e = 0; 7.5 saturates to 6 (0x7)
+    # block 2 amax 1.0: e = -2 (code 125); 1.0 -> 4 (0x6); 0.375 -> 1.5 (0x3);
+    #   -0.0625 -> -0.25 -> tie -> -0 (0x8)
+    # block 3 all zero: code 0, codes 0
+    W = np.zeros((32, 128), np.float32)
+    W[0, :32] = row_with([6.0, 5.0, -1.5], 32)
+    W[0, 32:64] = row_with([7.5], 32)
+    W[0, 64:96] = row_with([1.0, 0.375, -0.0625], 32)
+    codes, sc = Q.quantize_mxfp4(bf16(W))
+    assert sc[0].tolist() == [127, 127, 125, 0]
+    assert codes[0, :3].tolist() == [0x7, 0x6, 0xB]
+    assert codes[0, 32] == 0x7
+    assert codes[0, 64:67].tolist() == [0x6, 0x3, 0x8]
+    assert not codes[0, 96:].any()
+
+
+def test_mxfp4_invariants():
+    W = synth.linear_weight(64, 512, 11)
+    codes, sc = Q.quantize_mxfp4(W)
+    w = C.bf16_to_f32(W).reshape(64, 16, 32).astype(np.float64)
+    ab = np.abs(w).max(axis=2)
+    e = sc.astype(np.int64) - 127
+    r = ab / np.exp2(e)
+    assert np.all((r >= 4) & (r < 8))
+    top = np.abs(C.e2m1_decode(codes)).reshape(64, 16, 32).max(axis=2)
+    assert set(np.unique(top)) <= {4.0, 6.0}
+    # the workload's weights (|w| < 1/sqrt(3072)) sit near e = -8
+    assert np.all(e <= -6)
+
+
+def test_mxfp4_shape_rule():
+    with pytest.raises(ValueError):
+        Q.quantize_mxfp4(np.zeros((32, 48), np.uint16))
+
+
+# ------------------------------------------------------------------ packing and bf16 dequant
+
+
+def test_pack_bytes_and_roundtrip():
+    c = np.array([[1, 2, 15, 8]], np.uint8)
+    assert Q.pack_nibbles(c).tolist() == [[0x21, 0x8F]]
+    assert Q.pack_nibbles(np.array([[-1, 7]], np.int8)).tolist() == [[0x7F]]
+    rng = np.random.default_rng(3)
+    cc = rng.integers(0, 16, (8, 64)).astype(np.uint8)
+    assert np.array_equal(Q.unpack_nibbles(Q.pack_nibbles(cc)), cc)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp8", "nvfp4", "mxfp4"])
+def test_dequant_bf16_definition(fmt):
+    W = synth.linear_weight(32, 256, 12)
+    codes, s, g = Q.quantize(fmt, W)
+    got = Q.dequant_bf16(fmt, codes, s, g)
+    exact = Q.dequant(fmt, codes, s, g)
+    # int4 / mxfp4 products are exact in fp32 and bf16-representable
+    # (<= 11 resp. 2 significant bits): a single bf16 rounding of the exact value
+    if fmt in ("int4", "mxfp4"):
+        assert np.array_equal(got, C.f64_to_bf16(exact))
+    # every format: within one bf16 rounding (plus fp32 rounding) of the exact value
+    back = C.bf16_to_f32(got).astype(np.float64)
+    assert np.all(np.abs(back - exact) <= np.abs(exact) * (2.0 ** -8 + 2.0 ** -23) + 1e-30)
