@@ -1,0 +1,205 @@
+/*
+ * wq.h -- C ABI of the MI355X (gfx950) weight-only low-bit quantized Linear
+ * and the static-FP8 Linear.
+ *
+ * What the library computes (the Torch-TensorRT "TorchAO ... (Linear)"
+ * tutorial pages are the source of the method; each entry point cites its page
+ * and section):
+ *   - weight quantizers for four packed formats and their nibble packing,
+ *   - y = x . deq(W)^T + b with the dequantization fused ahead of a bf16 matrix
+ *     multiply (the "DQ prologue into GEMM" of every weight-only page),
+ *   - the static-FP8 path: absmax calibration, per-tensor activation
+ *     quantization to E4M3 and an FP8 x FP8 GEMM.
+ *
+ * Conventions for every entry point
+ *   - Shapes follow nn.Linear(in_features=K, out_features=N): weights W[N][K]
+ *     (rows contiguous along K), activations X[M][K], outputs Y[M][N]; all
+ *     row-major and contiguous.  bf16 is stored as uint16 bit patterns.
+ *   - Every pointer is a DEVICE pointer, allocated and owned by the caller.  The
+ *     library never allocates or frees device memory and keeps no pointer after
+ *     a call returns.  Scales, including the NVFP4 global scale and static-FP8
+ *     activation scales, stay on the device (no host synchronisation).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it; calls return without waiting for the GPU.
+ *   - The return value reports host-side validation and the launch itself
+ *     (hipGetLastError), not kernel completion.  Nothing is enqueued when a
+ *     check fails.  wq_last_error() gives a readable reason for the last
+ *     non-OK status on the calling thread.  No call throws or aborts.
+ *   - M == 0 or N == 0 is a valid empty call (nothing is launched).
+ *   - Base pointers of X, W/codes/packed and Y must be 16-byte aligned.
+ *
+ * Formats (scale layouts are row-major):
+ *   WQ_BF16  dense bf16 weight W[N][K] (the unquantized Linear; no scales)
+ *   WQ_INT4  symmetric group-wise INT4, group 128 along K, zero-point 0;
+ *            codes int8 [N][K] (-8..7), packed uint8 [N][K/2],
+ *            scales bf16 [N][K/128]
+ *   WQ_FP8   E4M3 (OCP, max 448) codes uint8 [N][K], one fp32 scale per
+ *            output row: scales float [N]
+ *   WQ_NVFP4 E2M1 codes (one per byte) [N][K], packed [N][K/2],
+ *            E4M3 block scales uint8 [N][K/16], one fp32 global scale
+ *   WQ_MXFP4 E2M1 codes [N][K], packed [N][K/2], E8M0 block scales
+ *            uint8 [N][K/32]
+ * Packing: byte j of a packed row holds element 2j in its low nibble and
+ * element 2j+1 in its high nibble.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WQ_ABI_VERSION 1
+
+typedef enum wq_format {
+  WQ_BF16 = 0,
+  WQ_INT4 = 1,
+  WQ_FP8 = 2,
+  WQ_NVFP4 = 3,
+  WQ_MXFP4 = 4
+} wq_format;
+
+typedef enum wq_status {
+  WQ_OK = 0,
+  WQ_EINVAL = 1,       /* null pointer, negative size, unknown format        */
+  WQ_ESHAPE = 2,       /* a format's divisibility rule is violated           */
+  WQ_EALIGN = 3,       /* a base pointer is not 16-byte aligned              */
+  WQ_EUNSUPPORTED = 4, /* valid for the format, not supported by the kernels */
+  WQ_EWORKSPACE = 5,   /* workspace missing or too small                     */
+  WQ_EHIP = 6          /* the HIP runtime reported an error                  */
+} wq_status;
+
+/* ABI version of the loaded library (WQ_ABI_VERSION at build time). */
+int wq_abi_version(void);
+
+/* Static string naming a status code. */
+const char* wq_status_str(int status);
+
+/* Reason for the last non-OK status returned on the calling thread ("" if none). */
+const char* wq_last_error(void);
+
+/*
+ * Byte sizes of the buffers of format `fmt` for a weight W[N][K]:
+ *   codes_bytes  : unpacked codes, one per byte (N*K; BF16: 2*N*K)
+ *   packed_bytes : what wq_linear reads (N*K/2 for 4-bit formats, N*K for FP8,
+ *                  2*N*K for BF16)
+ *   scale_bytes  : block/row scales (0 for BF16)
+ *   global_bytes : 4 for NVFP4's global scale, else 0
+ * Any output pointer may be NULL.  Returns WQ_ESHAPE if (N, K) break the
+ * format's divisibility rule.
+ */
+wq_status wq_layout(int fmt, int64_t N, int64_t K, size_t* codes_bytes, size_t* packed_bytes,
+                    size_t* scale_bytes, size_t* global_bytes);
+
+/*
+ * Quantize a bf16 weight W[N][K] to unpacked codes (one per byte) and scales.
+ *   INT4  -- "TorchAO INT4 Weight-Only Quantization (Linear)", intro and
+ *            "Define a linear model and quantize weights to symmetric INT4":
+ *            symmetric, zero-point 0, group 128.  s = bf16(max|w_group| / 7),
+ *            code = clamp(round(w / s), -8, 7) (the division uses the bf16
+ *            scale); an all-zero group has s = 0 and codes 0.  K % 128 == 0.
+ *   FP8   -- "TorchAO FP8 Weight-Only Quantization (Linear)", intro: per-row
+ *            s = max|w_row| / 448, code = E4M3(clamp(w / s, +-448)).
+ *   NVFP4 -- "TorchAO NVFP4 Weight-Only Quantization (Linear)", intro: with
+ *            A = max|W|, g = A / 2688; per 16-element block t = (amax/6)/g,
+ *            scale = E4M3(clamp(t, 2^-9, 448)), S = dec(scale) * g,
+ *            code = E2M1(clamp(w / S, +-6)).  N % 16 == 0 and K % 16 == 0.
+ *            `global_scale` (1 float, device) receives g.
+ *   MXFP4 -- "TorchAO MXFP4 Dynamic Activation + MX Weight (Linear)", intro:
+ *            per 32-element block e = floor(log2 amax) - 2 clamped to
+ *            [-127, 127] (an all-zero block gets -127), scale code e + 127,
+ *            code = E2M1(clamp(w / 2^e, +-6)).  N % 32 == 0 and K % 32 == 0.
+ * Every step is an IEEE fp32 operation and every cast rounds to nearest-even
+ * after clamping, keeping the sign of zero.  `global_scale` must be NULL for
+ * formats other than NVFP4.  WQ_BF16 is rejected (WQ_EINVAL).
+ */
+wq_status wq_quantize(int fmt, const void* W, int64_t N, int64_t K, void* codes, void* scales,
+                      float* global_scale, void* stream);
+
+/*
+ * Pack unpacked codes into the byte stream wq_linear reads
+ * ("TorchAO INT4 Weight-Only Quantization (Linear)", "Export and compile":
+ * one-code-per-byte int8 data re-packed into a 4-bit constant).  4-bit formats:
+ * two codes per byte, low nibble = even element; FP8: a plain copy.
+ * Packing is done once; there is no in-place update of a packed weight.
+ */
+wq_status wq_pack(int fmt, const void* codes, int64_t N, int64_t K, void* packed, void* stream);
+
+/*
+ * Dequantize packed weights to bf16 W_out[N][K] (the DQ of the two-kernel form,
+ * "TorchAO FP8 Weight-Only Quantization (Linear)", intro).  Each element is
+ * bf16(fp32 product) of the code's value and its scale(s), evaluated in the
+ * order code * block-scale * global-scale.
+ */
+wq_status wq_dequantize(int fmt, const void* packed, const void* scales, const float* global_scale,
+                        int64_t N, int64_t K, void* W_out, void* stream);
+
+/*
+ * Workspace bytes wq_linear / wq_fp8_static_linear need for (M, N, K); 0 means
+ * none.  The workspace must be zero-filled before its first use; every call
+ * returns the counters it uses to zero before the call's last kernel ends, so
+ * the same buffer serves later calls in stream order.  Calls that may run
+ * concurrently (different streams) need different workspaces.
+ */
+size_t wq_linear_workspace(int fmt, int64_t M, int64_t N, int64_t K);
+
+/*
+ * Y[M][N] = bf16( X[M][K] . deq(W)^T (+ bias[N]) ), fp32 accumulation, bias
+ * added in fp32, one round-to-nearest-even to bf16.  The weight stays packed
+ * in device memory and is dequantized in registers ahead of the bf16 matrix
+ * cores (every weight-only page's intro: a DQ prologue into a high-precision
+ * GEMM; activations stay bf16).
+ *   packed       : packed codes as wq_pack writes them (BF16: the dense weight)
+ *   scales       : the format's scales (NULL for BF16)
+ *   global_scale : NVFP4's device float, else NULL
+ *   bias         : bf16 [N] or NULL
+ * Kernel constraints: K % 32 == 0 for 4-bit formats, K % 16 for FP8, K % 8
+ * for BF16 (WQ_EUNSUPPORTED otherwise).
+ */
+wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* packed, const void* scales,
+                    const float* global_scale, const void* bias, int64_t N, void* Y, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Calibration observer ("TorchAO Static FP8 Quantization (Linear)", "Calibrate,
+ * then insert static FP8 Q/DQ": per-tensor activation min/max over the
+ * calibration forwards, read symmetrically): amax = max(amax, max|X|) over
+ * `numel` bf16 values.  `amax` (1 float, device) must start at 0 before the
+ * first batch.
+ */
+wq_status wq_absmax(const void* X, int64_t numel, float* amax, void* stream);
+
+/* scale[i] = fp32(amax[i] / 448) for i < count (device arrays). */
+wq_status wq_fp8_scale(const float* amax, float* scale, int64_t count, void* stream);
+
+/*
+ * Static activation Q ("TorchAO Static FP8 Quantization (Linear)", intro and
+ * "Graph after export" figure: bf16 activation -> Q -> FP8):
+ * Xq = E4M3(clamp(fp32(x / act_scale), +-448)), nearest-even; act_scale is one
+ * device float.  X bf16 [M][K] -> Xq uint8 [M][K].
+ */
+wq_status wq_fp8_quantize_act(const void* X, int64_t M, int64_t K, const float* act_scale, void* Xq,
+                              void* stream);
+
+/*
+ * Static-FP8 Linear (same page, intro: after Q/DQ fusion the GEMM itself runs
+ * in FP8): quantizes X with wq_fp8_quantize_act's rule, multiplies E4M3 x E4M3
+ * on the FP8 matrix cores with fp32 accumulation, then
+ * Y = bf16(acc * act_scale * w_scale[n] (+ bias[n])).
+ * Wq: E4M3 codes [N][K] (wq_quantize(WQ_FP8) output), w_scale: float [N].
+ * K % 16 == 0.  Workspace: wq_linear_workspace(WQ_FP8, M, N, K) plus M*K bytes
+ * for the quantized activations -- query wq_fp8_static_workspace.
+ */
+size_t wq_fp8_static_workspace(int64_t M, int64_t N, int64_t K);
+wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float* act_scale, const void* Wq,
+                               const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

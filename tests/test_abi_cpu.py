@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every symbol include/wq.h declares, and
+rejects bad arguments on the host before touching HIP (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+wq = pytest.importorskip("weight_only_bit_dequant_amd.wq")
+
+if not os.path.exists(wq.LIB_PATH):  # pragma: no cover
+    pytest.skip("libwq.so not built", allow_module_level=True)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = wq.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    L = wq.lib()
+    assert L.wq_abi_version() == 1
+    assert L.wq_status_str(0) == b"WQ_OK"
+    assert L.wq_status_str(2) == b"WQ_ESHAPE"
+    assert L.wq_status_str(99) == b"WQ_UNKNOWN"
+
+
+def test_layout_sizes():
+    assert wq.wq_layout("int4", 4096, 3072) == (4096 * 3072, 4096 * 1536, 4096 * 24 * 2, 0)
+    assert wq.wq_layout("fp8", 4096, 3072) == (4096 * 3072, 4096 * 3072, 4096 * 4, 0)
+    assert wq.wq_layout("nvfp4", 4096, 3072) == (4096 * 3072, 4096 * 1536, 4096 * 192, 4)
+    assert wq.wq_layout("mxfp4", 4096, 3072) == (4096 * 3072, 4096 * 1536, 4096 * 96, 0)
+    assert wq.wq_layout("bf16", 8, 16) == (256, 256, 0, 0)
+
+
+@pytest.mark.parametrize("fmt,N,K", [("int4", 64, 100), ("nvfp4", 40, 64), ("nvfp4", 64, 40), ("mxfp4", 48, 64),
+                                     ("mxfp4", 64, 48)])
+def test_shape_rules(fmt, N, K):
+    with pytest.raises(ValueError) as e:
+        wq.wq_layout(fmt, N, K)
+    assert e.value.status == wq.ESHAPE
+
+
+def _call_linear(fmt=1, X=16, M=32, K=256, W=32, S=48, G=None, B=None, N=64, Y=64, ws=None, wsb=0):
+    L = wq.lib()
+    v = ctypes.c_void_p
+    return L.wq_linear(fmt, v(X), M, K, v(W), v(S), v(G), v(B), N, v(Y), v(ws), wsb, None)
+
+
+def test_linear_host_validation():
+    # pointers below are fake; every call fails validation before any HIP call
+    assert _call_linear(fmt=9) == wq.EINVAL
+    assert _call_linear(M=-1) == wq.EINVAL
+    assert _call_linear(K=100) == wq.ESHAPE  # INT4 group
+    assert _call_linear(fmt=3, N=40, G=64) == wq.ESHAPE  # NVFP4 %16
+    assert _call_linear(fmt=4, K=48) == wq.ESHAPE  # MXFP4 %32
+    assert _call_linear(fmt=2, K=24) == wq.EUNSUPPORTED  # FP8 kernel needs K % 16
+    assert _call_linear(fmt=3, K=48, N=64, G=64) == wq.EUNSUPPORTED  # NVFP4 kernel needs K % 32
+    assert _call_linear(X=None) == wq.EINVAL
+    assert _call_linear(S=None) == wq.EINVAL
+    assert _call_linear(fmt=3, G=None) == wq.EINVAL  # NVFP4 needs its global scale
+    assert _call_linear(fmt=1, G=64) == wq.EINVAL  # global scale only for NVFP4
+    assert _call_linear(X=24) == wq.EALIGN
+    assert _call_linear(Y=8) == wq.EALIGN
+    # M = 0 and N = 0 are empty calls (nothing launched)
+    assert _call_linear(M=0) == wq.OK
+    assert _call_linear(N=0) == wq.OK
+    # split-K needs a workspace: 4096x3072 at M=32 plans several K splits
+    need = wq.wq_linear_workspace("int4", 32, 4096, 3072)
+    assert need > 0
+    assert _call_linear(M=32, K=3072, N=4096, ws=None) == wq.EWORKSPACE
+    assert _call_linear(M=32, K=3072, N=4096, ws=64, wsb=need - 1) == wq.EWORKSPACE
+    assert b"workspace" in wq.lib().wq_last_error()
+
+
+def test_quantize_pack_dequant_validation():
+    L = wq.lib()
+    v = ctypes.c_void_p
+    assert L.wq_quantize(0, v(16), 64, 64, v(16), v(16), None, None) == wq.EINVAL  # BF16 has no quantizer
+    assert L.wq_quantize(3, v(16), 64, 64, v(16), v(16), None, None) == wq.EINVAL  # NVFP4 needs global
+    assert L.wq_quantize(1, v(16), 64, 64, v(16), v(16), None, None) == wq.ESHAPE
+    assert L.wq_quantize(4, v(8), 64, 64, v(16), v(16), None, None) == wq.EALIGN
+    assert L.wq_quantize(2, None, 64, 64, v(16), v(16), None, None) == wq.EINVAL
+    assert L.wq_quantize(2, None, 0, 64, None, None, None, None) == wq.OK
+    assert L.wq_pack(0, v(16), 64, 64, v(16), None) == wq.EINVAL
+    assert L.wq_pack(4, v(16), 64, 40, v(16), None) == wq.ESHAPE
+    assert L.wq_dequantize(3, v(16), v(16), None, 64, 64, v(16), None) == wq.EINVAL
+    assert L.wq_dequantize(2, v(16), v(16), None, 64, 12, v(16), None) == wq.EUNSUPPORTED
+    assert L.wq_fp8_quantize_act(v(16), 4, 16, None, v(16), None) == wq.EINVAL
+    assert L.wq_fp8_static_linear(v(16), 4, 24, v(16), v(16), v(16), None, 16, v(16), v(16), 1 << 20,
+                                  None) == wq.EUNSUPPORTED
+    assert L.wq_fp8_static_linear(v(16), 4, 32, v(16), v(16), v(16), None, 16, v(16), None, 0,
+                                  None) == wq.EWORKSPACE
+    assert L.wq_absmax(None, 10, v(16), None) == wq.EINVAL
+    assert L.wq_absmax(None, 0, None, None) == wq.OK
+
+
+def test_workspace_plans_are_consistent():
+    # empty or invalid problems need no workspace; the static path adds the
+    # quantized-activation buffer (M*K rounded to 256) to the GEMM's
+    assert wq.wq_linear_workspace("int4", 0, 4096, 3072) == 0
+    assert wq.wq_linear_workspace(9, 32, 4096, 3072) == 0
+    M, N, K = 32, 4096, 3072
+    gemm = wq.wq_linear_workspace("fp8", M, N, K)
+    assert wq.wq_fp8_static_workspace(M, N, K) >= gemm + M * K
+    # large M has enough workgroups without K splits
+    assert wq.wq_linear_workspace("mxfp4", 4096, 4096, 3072) == 0

@@ -1,0 +1,269 @@
+// C ABI (include/wq.h): argument validation, layout queries and dispatch to
+// the kernel launchers.  Host-side checks run before any HIP call, so every
+// error path is reachable without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "wq.h"
+#include "wq_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+wq_status fail(wq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+wq_status ok() {
+  g_err[0] = 0;
+  return WQ_OK;
+}
+
+wq_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(WQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+const char* fmt_name(int f) {
+  switch (f) {
+    case WQ_BF16: return "BF16";
+    case WQ_INT4: return "INT4";
+    case WQ_FP8: return "FP8";
+    case WQ_NVFP4: return "NVFP4";
+    case WQ_MXFP4: return "MXFP4";
+    default: return "?";
+  }
+}
+
+bool valid_fmt(int f) { return f >= WQ_BF16 && f <= WQ_MXFP4; }
+
+// Divisibility rules of each format (INT4: group 128 along K; NVFP4: last two
+// weight dims % 16; MXFP4: K and N % 32).
+wq_status check_shape_rule(int f, int64_t N, int64_t K) {
+  if (N < 0 || K < 0) return fail(WQ_EINVAL, "negative size N=%lld K=%lld", (long long)N, (long long)K);
+  if (f == WQ_INT4 && K % 128) return fail(WQ_ESHAPE, "INT4 needs K %% 128 == 0 (K=%lld)", (long long)K);
+  if (f == WQ_NVFP4 && (N % 16 || K % 16))
+    return fail(WQ_ESHAPE, "NVFP4 needs N %% 16 == 0 and K %% 16 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
+  if (f == WQ_MXFP4 && (N % 32 || K % 32))
+    return fail(WQ_ESHAPE, "MXFP4 needs N %% 32 == 0 and K %% 32 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
+  return WQ_OK;
+}
+
+int kernel_k_multiple(int f) {
+  switch (f) {
+    case WQ_BF16: return 8;
+    case WQ_FP8: return 16;
+    default: return 32;
+  }
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+int wq_abi_version(void) { return WQ_ABI_VERSION; }
+
+const char* wq_status_str(int s) {
+  switch (s) {
+    case WQ_OK: return "WQ_OK";
+    case WQ_EINVAL: return "WQ_EINVAL";
+    case WQ_ESHAPE: return "WQ_ESHAPE";
+    case WQ_EALIGN: return "WQ_EALIGN";
+    case WQ_EUNSUPPORTED: return "WQ_EUNSUPPORTED";
+    case WQ_EWORKSPACE: return "WQ_EWORKSPACE";
+    case WQ_EHIP: return "WQ_EHIP";
+    default: return "WQ_UNKNOWN";
+  }
+}
+
+const char* wq_last_error(void) { return g_err; }
+
+wq_status wq_layout(int fmt, int64_t N, int64_t K, size_t* codes_bytes, size_t* packed_bytes,
+                    size_t* scale_bytes, size_t* global_bytes) {
+  if (!valid_fmt(fmt)) return fail(WQ_EINVAL, "unknown format %d", fmt);
+  wq_status st = check_shape_rule(fmt, N, K);
+  if (st != WQ_OK) return st;
+  const size_t nk = (size_t)N * (size_t)K;
+  size_t cb = 0, pb = 0, sb = 0, gb = 0;
+  switch (fmt) {
+    case WQ_BF16: cb = pb = 2 * nk; break;
+    case WQ_INT4: cb = nk; pb = nk / 2; sb = (size_t)N * (size_t)(K / 128) * 2; break;
+    case WQ_FP8: cb = pb = nk; sb = (size_t)N * 4; break;
+    case WQ_NVFP4: cb = nk; pb = nk / 2; sb = (size_t)N * (size_t)(K / 16); gb = 4; break;
+    case WQ_MXFP4: cb = nk; pb = nk / 2; sb = (size_t)N * (size_t)(K / 32); break;
+  }
+  if (codes_bytes) *codes_bytes = cb;
+  if (packed_bytes) *packed_bytes = pb;
+  if (scale_bytes) *scale_bytes = sb;
+  if (global_bytes) *global_bytes = gb;
+  return ok();
+}
+
+wq_status wq_quantize(int fmt, const void* W, int64_t N, int64_t K, void* codes, void* scales,
+                      float* global_scale, void* stream) {
+  if (!valid_fmt(fmt) || fmt == WQ_BF16) return fail(WQ_EINVAL, "wq_quantize: unsupported format %d", fmt);
+  wq_status st = check_shape_rule(fmt, N, K);
+  if (st != WQ_OK) return st;
+  if (N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (N == 0 || K == 0) return ok();
+  if (!W || !codes || !scales) return fail(WQ_EINVAL, "wq_quantize: null pointer");
+  if ((fmt == WQ_NVFP4) != (global_scale != nullptr))
+    return fail(WQ_EINVAL, "wq_quantize: global_scale is required for NVFP4 and must be NULL otherwise");
+  if (!aligned16(W) || !aligned16(codes)) return fail(WQ_EALIGN, "wq_quantize: W and codes must be 16-byte aligned");
+  return hip_status(wq::launch_quantize(fmt, (const uint16_t*)W, N, K, codes, scales, global_scale,
+                                        (hipStream_t)stream),
+                    "wq_quantize launch");
+}
+
+wq_status wq_pack(int fmt, const void* codes, int64_t N, int64_t K, void* packed, void* stream) {
+  if (!valid_fmt(fmt) || fmt == WQ_BF16) return fail(WQ_EINVAL, "wq_pack: unsupported format %d", fmt);
+  wq_status st = check_shape_rule(fmt, N, K);
+  if (st != WQ_OK) return st;
+  if (N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (N == 0 || K == 0) return ok();
+  if (!codes || !packed) return fail(WQ_EINVAL, "wq_pack: null pointer");
+  if (!aligned16(codes) || !aligned16(packed)) return fail(WQ_EALIGN, "wq_pack: buffers must be 16-byte aligned");
+  const int64_t nk = N * K;
+  if (fmt == WQ_FP8 ? (nk % 16) : (nk % 32))
+    return fail(WQ_EUNSUPPORTED, "wq_pack: N*K must be a multiple of %d", fmt == WQ_FP8 ? 16 : 32);
+  return hip_status(wq::launch_pack(fmt, (const uint8_t*)codes, N, K, (uint8_t*)packed, (hipStream_t)stream),
+                    "wq_pack launch");
+}
+
+wq_status wq_dequantize(int fmt, const void* packed, const void* scales, const float* global_scale,
+                        int64_t N, int64_t K, void* W_out, void* stream) {
+  if (!valid_fmt(fmt)) return fail(WQ_EINVAL, "wq_dequantize: unknown format %d", fmt);
+  wq_status st = check_shape_rule(fmt, N, K);
+  if (st != WQ_OK) return st;
+  if (N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (N == 0 || K == 0) return ok();
+  if (!packed || !W_out || (fmt != WQ_BF16 && !scales)) return fail(WQ_EINVAL, "wq_dequantize: null pointer");
+  if (fmt == WQ_NVFP4 && !global_scale) return fail(WQ_EINVAL, "wq_dequantize: NVFP4 needs global_scale");
+  if (K % 8) return fail(WQ_EUNSUPPORTED, "wq_dequantize: K %% 8 != 0");
+  if (!aligned16(packed) || !aligned16(W_out)) return fail(WQ_EALIGN, "wq_dequantize: buffers must be 16-byte aligned");
+  return hip_status(wq::launch_dequantize(fmt, packed, scales, global_scale, N, K, (uint16_t*)W_out,
+                                          (hipStream_t)stream),
+                    "wq_dequantize launch");
+}
+
+size_t wq_linear_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (!valid_fmt(fmt) || M <= 0 || N <= 0 || K <= 0) return 0;
+  return wq::plan_linear(fmt, M, N, K).ws_bytes;
+}
+
+static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int64_t K, const void* W,
+                               const void* scales, const float* gscale, const float* act_scale, const void* bias,
+                               int64_t N, void* Y, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_fmt(fmt)) return fail(WQ_EINVAL, "unknown format %d", fmt);
+  if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
+  wq_status st = check_shape_rule(fmt, N, K);
+  if (st != WQ_OK) return st;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (M == 0 || N == 0) return ok();
+  if (K == 0) return fail(WQ_EUNSUPPORTED, "K == 0");
+  if (K % kernel_k_multiple(fmt))
+    return fail(WQ_EUNSUPPORTED, "%s linear kernels need K %% %d == 0 (K=%lld)", fmt_name(fmt),
+                kernel_k_multiple(fmt), (long long)K);
+  if (!X || !W || !Y) return fail(WQ_EINVAL, "null X, weight or Y");
+  if (fmt != WQ_BF16 && !scales) return fail(WQ_EINVAL, "null scales");
+  if (kfmt == wq::KF_NVFP4 && !gscale) return fail(WQ_EINVAL, "NVFP4 needs global_scale");
+  if (kfmt != wq::KF_NVFP4 && gscale) return fail(WQ_EINVAL, "global_scale must be NULL for %s", fmt_name(fmt));
+  if (kfmt == wq::KF_FP8S && !act_scale) return fail(WQ_EINVAL, "null act_scale");
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return fail(WQ_EALIGN, "X, weight and Y must be 16-byte aligned");
+  const wq::LinearPlan p = wq::plan_linear(kfmt, M, N, K);
+  if (p.ws_bytes > 0) {
+    if (!ws || ws_bytes < p.ws_bytes)
+      return fail(WQ_EWORKSPACE, "workspace of %zu bytes required (got %zu)", p.ws_bytes, ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(WQ_EALIGN, "workspace must be 16-byte aligned");
+  }
+  wq::LinearArgs a{};
+  a.X = X;
+  a.W = W;
+  a.scales = scales;
+  a.gscale = gscale;
+  a.act_scale = act_scale;
+  a.bias = (const uint16_t*)bias;
+  a.Y = (uint16_t*)Y;
+  a.part = p.ws_bytes ? (float*)ws : nullptr;
+  a.cnt = p.ws_bytes ? (unsigned*)((char*)ws + p.part_bytes) : nullptr;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  return hip_status(wq::launch_linear(kfmt, a, p, (hipStream_t)stream), "wq_linear launch");
+}
+
+wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* packed, const void* scales,
+                    const float* global_scale, const void* bias, int64_t N, void* Y, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return linear_common(fmt, fmt, X, M, K, packed, scales, global_scale, nullptr, bias, N, Y, workspace,
+                       workspace_bytes, stream);
+}
+
+wq_status wq_absmax(const void* X, int64_t numel, float* amax, void* stream) {
+  if (numel < 0) return fail(WQ_EINVAL, "negative numel");
+  if (numel == 0) return ok();
+  if (!X || !amax) return fail(WQ_EINVAL, "wq_absmax: null pointer");
+  return hip_status(wq::launch_absmax((const uint16_t*)X, numel, amax, (hipStream_t)stream), "wq_absmax launch");
+}
+
+wq_status wq_fp8_scale(const float* amax, float* scale, int64_t count, void* stream) {
+  if (count < 0) return fail(WQ_EINVAL, "negative count");
+  if (count == 0) return ok();
+  if (!amax || !scale) return fail(WQ_EINVAL, "wq_fp8_scale: null pointer");
+  return hip_status(wq::launch_fp8_scale(amax, scale, count, (hipStream_t)stream), "wq_fp8_scale launch");
+}
+
+wq_status wq_fp8_quantize_act(const void* X, int64_t M, int64_t K, const float* act_scale, void* Xq,
+                              void* stream) {
+  if (M < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
+  if (M > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (M == 0 || K == 0) return ok();
+  if (!X || !Xq || !act_scale) return fail(WQ_EINVAL, "wq_fp8_quantize_act: null pointer");
+  if (!aligned16(X) || !aligned16(Xq)) return fail(WQ_EALIGN, "X and Xq must be 16-byte aligned");
+  return hip_status(wq::launch_quantize_act((const uint16_t*)X, M * K, act_scale, (uint8_t*)Xq,
+                                            (hipStream_t)stream),
+                    "wq_fp8_quantize_act launch");
+}
+
+size_t wq_fp8_static_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return align256((size_t)M * (size_t)K) + wq::plan_linear(wq::KF_FP8S, M, N, K).ws_bytes;
+}
+
+wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float* act_scale, const void* Wq,
+                               const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
+  if (M == 0 || N == 0) return ok();
+  if (K > 0 && K % 16) return fail(WQ_EUNSUPPORTED, "static FP8 linear needs K %% 16 == 0 (K=%lld)", (long long)K);
+  const size_t need = wq_fp8_static_workspace(M, N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(WQ_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(WQ_EALIGN, "workspace must be 16-byte aligned");
+  if (K == 0) return fail(WQ_EUNSUPPORTED, "K == 0");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (!X || !act_scale || !Wq || !w_scale || !Y) return fail(WQ_EINVAL, "wq_fp8_static_linear: null pointer");
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(Y))
+    return fail(WQ_EALIGN, "X, Wq and Y must be 16-byte aligned");
+  const size_t xq_bytes = align256((size_t)M * (size_t)K);
+  wq_status st = wq_fp8_quantize_act(X, M, K, act_scale, workspace, stream);
+  if (st != WQ_OK) return st;
+  return linear_common(wq::KF_FP8S, WQ_FP8, workspace, M, K, Wq, w_scale, nullptr, act_scale, bias, N, Y,
+                       (char*)workspace + xq_bytes, workspace_bytes - xq_bytes, stream);
+}
+
+}  // extern "C"

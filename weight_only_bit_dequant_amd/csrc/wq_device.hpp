@@ -1,0 +1,108 @@
+// Device-side element codecs and small helpers for gfx950.
+//
+// Encoders are written on the fp32 bit pattern with integer round-to-nearest-
+// even, so that quantized codes are bit-identical to an IEEE reference: every
+// value is clamped to the format's largest finite magnitude first, the sign bit
+// is kept (a negative zero or a negative value that rounds to zero gives the
+// negative-zero code).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// bf16 (bit pattern) -> fp32, exact.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return bitsf(((uint32_t)h) << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = fbits(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Round the integer `mant` (the dropped low bits are `drop` wide) to nearest
+// even; returns the kept value (may carry to 1 << (23 - drop)).
+__device__ __forceinline__ uint32_t rne_shift(uint32_t mant, int drop) {
+  uint32_t kept = mant >> drop;
+  uint32_t rem = mant & ((1u << drop) - 1u);
+  uint32_t half = 1u << (drop - 1);
+  return kept + ((rem > half) || (rem == half && (kept & 1u)));
+}
+
+// E4M3 ("fn", bias 7, max 448): x must already be clamped to [-448, 448].
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  uint32_t u = fbits(x);
+  uint32_t sign = (u >> 31) << 7;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3C800000u) {  // |x| < 2^-6: subnormal grid of 2^-9 (exact scaling)
+    code = (uint32_t)__builtin_rintf(bitsf(a) * 512.0f);
+  } else {
+    int e = (int)(a >> 23) - 127;  // -6 .. 8
+    uint32_t m = rne_shift(a & 0x7FFFFFu, 20);
+    if (m == 8u) { m = 0u; e += 1; }
+    code = ((uint32_t)(e + 7) << 3) | m;
+  }
+  return sign | code;
+}
+
+// E2M1 (bias 1, max 6): x must already be clamped to [-6, 6].
+__device__ __forceinline__ uint32_t e2m1_encode(float x) {
+  uint32_t u = fbits(x);
+  uint32_t sign = (u >> 31) << 3;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3F800000u) {  // |x| < 1: subnormal grid of 0.5
+    code = (uint32_t)__builtin_rintf(bitsf(a) * 2.0f);
+  } else {
+    int e = (int)(a >> 23) - 127;  // 0 .. 2
+    uint32_t m = rne_shift(a & 0x7FFFFFu, 22);
+    if (m == 2u) { m = 0u; e += 1; }
+    code = ((uint32_t)(e + 1) << 1) | m;
+  }
+  return sign | code;
+}
+
+// Decoders (exact).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = (e == 0u) ? (float)m * 0.001953125f  // m * 2^-9
+                        : bitsf(((e + 120u) << 23) | (m << 20));
+  if ((c & 0x7Fu) == 0x7Fu) mag = __builtin_nanf("");
+  return (c & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+  const float t[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  float v = t[c & 7u];
+  return (c & 8u) ? -v : v;
+}
+
+// 2^(c - 127) for an E8M0 code (0xFF -> NaN).
+__device__ __forceinline__ float e8m0_decode(uint32_t c) {
+  if (c == 0xFFu) return __builtin_nanf("");
+  if (c == 0u) return bitsf(0x00400000u);  // 2^-127 (fp32 subnormal)
+  return bitsf(c << 23);
+}
+
+__device__ __forceinline__ float clampf(float x, float lo, float hi) { return fminf(fmaxf(x, lo), hi); }
+
+// Nonnegative float atomic max via the ordered integer view (valid for x >= 0, not NaN).
+__device__ __forceinline__ void atomic_max_nonneg(float* p, float x) {
+  atomicMax(reinterpret_cast<unsigned int*>(p), fbits(x));
+}
+
+}  // namespace wq

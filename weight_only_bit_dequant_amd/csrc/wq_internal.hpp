@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (wq_api.hip) and the kernels.
+// Launchers assume their arguments were validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wq {
+
+// Kernel-side format ids (the ABI's wq_format values plus the FP8-activation
+// variant used by the static path).
+enum KFmt { KF_BF16 = 0, KF_INT4 = 1, KF_FP8 = 2, KF_NVFP4 = 3, KF_MXFP4 = 4, KF_FP8S = 5 };
+
+// Launch plan of the small-M dequant-GEMM (shared by the workspace query and
+// the launch so both always agree).
+struct LinearPlan {
+  int mt;         // 16-row MFMA tiles per workgroup (1, 2 or 4)
+  int gx, gz;     // workgroups along N (64 columns each) and along M
+  int S;          // K splits across workgroups
+  int spw;        // K macro-steps per wave
+  size_t part_bytes, cnt_bytes, ws_bytes;
+};
+
+LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K);
+
+struct LinearArgs {
+  const void* X;         // bf16 [M][K], or E4M3 [M][K] for KF_FP8S
+  const void* W;         // packed weight
+  const void* scales;    // format scales
+  const float* gscale;   // NVFP4 global scale (device)
+  const float* act_scale;  // static FP8 activation scale (device)
+  const uint16_t* bias;  // bf16 [N] or null
+  uint16_t* Y;           // bf16 [M][N]
+  float* part;           // split-K partials (workspace)
+  unsigned* cnt;         // split-K arrival counters (workspace, zero between calls)
+  int M, N, K;
+};
+
+hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
+
+hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t N, int64_t K, void* codes, void* scales,
+                           float* gscale, hipStream_t s);
+hipError_t launch_pack(int fmt, const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
+hipError_t launch_dequantize(int fmt, const void* packed, const void* scales, const float* gscale, int64_t N,
+                             int64_t K, uint16_t* out, hipStream_t s);
+hipError_t launch_absmax(const uint16_t* X, int64_t numel, float* amax, hipStream_t s);
+hipError_t launch_fp8_scale(const float* amax, float* scale, int64_t count, hipStream_t s);
+hipError_t launch_quantize_act(const uint16_t* X, int64_t numel, const float* act_scale, uint8_t* Xq,
+                               hipStream_t s);
+
+}  // namespace wq

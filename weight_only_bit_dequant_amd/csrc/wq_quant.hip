@@ -1,0 +1,371 @@
+// Offline and calibration kernels: weight quantizers, packing, dequantization
+// to bf16, absmax observers and the static activation Q.
+//
+// Quantizer arithmetic is IEEE fp32 (correctly rounded division; the library
+// is built with -fhip-fp32-correctly-rounded-divide-sqrt and without
+// denormal flushing) followed by clamp-then-nearest-even casts, so codes and
+// scales are bit-identical to an IEEE reference.
+#include "wq_device.hpp"
+#include "wq_internal.hpp"
+
+namespace wq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+inline unsigned grid_for(int64_t items, int per_block = kThreads) {
+  int64_t g = (items + per_block - 1) / per_block;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+// 16 consecutive bf16 -> fp32 (two 16-byte loads).
+__device__ __forceinline__ void load16_bf16(const uint16_t* p, float* out) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  u32x4 a = q[0], b = q[1];
+  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    out[2 * i] = bitsf(w[i] << 16);
+    out[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u);
+  }
+}
+
+// ---------------------------------------------------------------- INT4
+// "TorchAO INT4 Weight-Only Quantization (Linear)": symmetric, zero-point 0,
+// group 128 along K.  One thread per (row, group).
+__global__ __launch_bounds__(kThreads) void k_quant_int4(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                                         int8_t* __restrict__ codes,
+                                                         uint16_t* __restrict__ scales) {
+  const int64_t G = K / 128;
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= N * G) return;
+  const int64_t n = id / G, gi = id % G;
+  const uint16_t* w = W + n * K + gi * 128;
+  float v[128];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load16_bf16(w + 16 * i, v + 16 * i);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 128; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint16_t sb = f32_to_bf16(amax / 7.0f);
+  const float s = bf16_to_f32(sb);
+  scales[n * G + gi] = sb;
+  uint32_t packed[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) packed[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 128; ++i) {
+    float q = (s > 0.f) ? v[i] / s : 0.f;
+    int c = (int)__builtin_rintf(q);
+    c = c < -8 ? -8 : (c > 7 ? 7 : c);
+    packed[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * (i & 3));
+  }
+  u32x4* out = reinterpret_cast<u32x4*>(codes + n * K + gi * 128);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = u32x4{packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]};
+}
+
+// ---------------------------------------------------------------- FP8 row
+// "TorchAO FP8 Weight-Only Quantization (Linear)": one fp32 scale per output
+// row, s = max|w| / 448.  One workgroup per row.
+__device__ __forceinline__ float block_max(float v, float* lds) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) lds[wv] = v;
+  __syncthreads();
+  float r = lds[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, lds[i]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_fp8row(const uint16_t* __restrict__ W, int64_t K,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ scales) {
+  __shared__ float lds[kThreads / 64];
+  const int64_t n = blockIdx.x;
+  const uint16_t* w = W + n * K;
+  float amax = 0.f;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) amax = fmaxf(amax, fabsf(bf16_to_f32(w[k])));
+  amax = block_max(amax, lds);
+  const float s = amax / 448.0f;
+  if (threadIdx.x == 0) scales[n] = s;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+    float x = bf16_to_f32(w[k]);
+    float q = (s > 0.f) ? x / s : x;
+    codes[n * K + k] = (uint8_t)e4m3_encode(clampf(q, -448.f, 448.f));
+  }
+}
+
+// ---------------------------------------------------------------- NVFP4
+// "TorchAO NVFP4 Weight-Only Quantization (Linear)": E2M1 codes, E4M3 scale per
+// 16 consecutive K, fp32 global scale g = max|W| / (448 * 6).
+__global__ void k_fill_f32(float* p, float v, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_absmax_bf16(const uint16_t* __restrict__ X, int64_t n,
+                                                          float* __restrict__ amax) {
+  __shared__ float lds[kThreads / 64];
+  float m = 0.f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+    m = fmaxf(m, fabsf(bf16_to_f32(X[i])));
+  m = block_max(m, lds);
+  if (threadIdx.x == 0) atomic_max_nonneg(amax, m);
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                                          const float* __restrict__ tensor_amax,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int64_t B = K / 16;
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= N * B) return;
+  const int64_t n = id / B, bi = id % B;
+  float v[16];
+  load16_bf16(W + n * K + bi * 16, v);
+  float ab = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
+  const float g = tensor_amax[0] / 2688.0f;
+  float t = (g > 0.f) ? (ab / 6.0f) / g : 0.f;
+  t = clampf(t, 0.001953125f, 448.f);
+  const uint32_t sc = e4m3_encode(t);
+  const float S = e4m3_decode(sc) * g;
+  scales[n * B + bi] = (uint8_t)sc;
+  uint32_t out[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float q = (S > 0.f) ? v[i] / S : v[i];
+    out[i >> 2] |= e2m1_encode(clampf(q, -6.f, 6.f)) << (8 * (i & 3));
+  }
+  *reinterpret_cast<u32x4*>(codes + n * K + bi * 16) = u32x4{out[0], out[1], out[2], out[3]};
+}
+
+__global__ void k_nvfp4_global(float* gscale) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) gscale[0] = gscale[0] / 2688.0f;
+}
+
+// ---------------------------------------------------------------- MXFP4
+// "TorchAO MXFP4 Dynamic Activation + MX Weight (Linear)": E2M1 codes, E8M0
+// scale per 32 consecutive K; shared exponent floor(log2 amax) - 2.
+__global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int64_t B = K / 32;
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= N * B) return;
+  const int64_t n = id / B, bi = id % B;
+  float v[32];
+  load16_bf16(W + n * K + bi * 32, v);
+  load16_bf16(W + n * K + bi * 32 + 16, v + 16);
+  float ab = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ab = fmaxf(ab, fabsf(v[i]));
+  const uint32_t ebits = fbits(ab) >> 23;  // biased exponent; 0 for zero and subnormals
+  int e = (ebits == 0u) ? -127 : (int)ebits - 127 - 2;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  scales[n * B + bi] = (uint8_t)(e + 127);
+  const float p = (e == -127) ? bitsf(0x00400000u) : bitsf((uint32_t)(e + 127) << 23);
+  uint32_t out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float q = v[i] / p;
+    out[i >> 2] |= e2m1_encode(clampf(q, -6.f, 6.f)) << (8 * (i & 3));
+  }
+  u32x4* o = reinterpret_cast<u32x4*>(codes + n * K + bi * 32);
+  o[0] = u32x4{out[0], out[1], out[2], out[3]};
+  o[1] = u32x4{out[4], out[5], out[6], out[7]};
+}
+
+// ---------------------------------------------------------------- packing
+// Two 4-bit codes per byte along K, even element in the low nibble.  One
+// thread per 16 output bytes (32 codes).
+__global__ __launch_bounds__(kThreads) void k_pack4(const uint8_t* __restrict__ codes, int64_t n16,
+                                                    uint8_t* __restrict__ packed) {
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= n16) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(codes + id * 32);
+  u32x4 a = src[0], b = src[1];
+  uint32_t in[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = in[2 * i], hi = in[2 * i + 1];
+    // bytes b0..b3 of lo -> two output bytes; same for hi
+    uint32_t r = 0;
+    r |= ((lo & 0xFu) | ((lo >> 4) & 0xF0u));
+    r |= (((lo >> 16) & 0xFu) | ((lo >> 20) & 0xF0u)) << 8;
+    r |= ((hi & 0xFu) | ((hi >> 4) & 0xF0u)) << 16;
+    r |= (((hi >> 16) & 0xFu) | ((hi >> 20) & 0xF0u)) << 24;
+    out[i] = r;
+  }
+  *reinterpret_cast<u32x4*>(packed + id * 16) = u32x4{out[0], out[1], out[2], out[3]};
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy16(const u32x4* __restrict__ src, int64_t n16,
+                                                     u32x4* __restrict__ dst) {
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id < n16) dst[id] = src[id];
+}
+
+// ---------------------------------------------------------------- dequantize to bf16
+// bf16(fp32(code value * block scale (* global))).  One thread per 8 outputs.
+template <int F>
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ P, const void* __restrict__ scales,
+                                                      const float* __restrict__ gscale, int64_t N, int64_t K,
+                                                      uint16_t* __restrict__ out) {
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t per_row = K / 8;
+  if (id >= N * per_row) return;
+  const int64_t n = id / per_row, k0 = (id % per_row) * 8;
+  uint16_t r[8];
+  if constexpr (F == KF_FP8) {
+    const float s = reinterpret_cast<const float*>(scales)[n];
+    const uint8_t* c = P + n * K + k0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = f32_to_bf16(e4m3_decode(c[i]) * s);
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(P + n * (K / 2) + k0 / 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = (w >> (4 * i)) & 0xFu;
+      float v;
+      if constexpr (F == KF_INT4) {
+        const float s = bf16_to_f32(reinterpret_cast<const uint16_t*>(scales)[n * (K / 128) + (k0 + i) / 128]);
+        v = (float)((int)c - ((c & 8u) ? 16 : 0)) * s;
+      } else if constexpr (F == KF_NVFP4) {
+        const float d = e4m3_decode(reinterpret_cast<const uint8_t*>(scales)[n * (K / 16) + (k0 + i) / 16]);
+        v = (e2m1_decode(c) * d) * gscale[0];
+      } else {  // MXFP4
+        const float p = e8m0_decode(reinterpret_cast<const uint8_t*>(scales)[n * (K / 32) + (k0 + i) / 32]);
+        v = e2m1_decode(c) * p;
+      }
+      r[i] = f32_to_bf16(v);
+    }
+  }
+  *reinterpret_cast<u32x4*>(out + n * K + k0) =
+      u32x4{r[0] | ((uint32_t)r[1] << 16), r[2] | ((uint32_t)r[3] << 16), r[4] | ((uint32_t)r[5] << 16),
+            r[6] | ((uint32_t)r[7] << 16)};
+}
+
+// ---------------------------------------------------------------- static FP8 helpers
+__global__ void k_fp8_scale(const float* __restrict__ amax, float* __restrict__ scale, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) scale[i] = amax[i] / 448.0f;
+}
+
+// "TorchAO Static FP8 Quantization (Linear)": x -> E4M3(clamp(x / act_scale, +-448)).
+// One thread per 8 elements; the tail (numel % 8) is handled element-wise.
+__global__ __launch_bounds__(kThreads) void k_quant_act(const uint16_t* __restrict__ X, int64_t numel,
+                                                        const float* __restrict__ act_scale,
+                                                        uint8_t* __restrict__ Xq) {
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const float s = act_scale[0];
+  const int64_t full = numel / 8;
+  if (id < full) {
+    u32x4 v = reinterpret_cast<const u32x4*>(X)[id];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = bitsf((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+      float q = (s > 0.f) ? x / s : x;
+      o[i >> 2] |= e4m3_encode(clampf(q, -448.f, 448.f)) << (8 * (i & 3));
+    }
+    reinterpret_cast<u32x2*>(Xq)[id] = u32x2{o[0], o[1]};
+  } else if (id == full) {
+    for (int64_t i = full * 8; i < numel; ++i) {
+      float x = bf16_to_f32(X[i]);
+      float q = (s > 0.f) ? x / s : x;
+      Xq[i] = (uint8_t)e4m3_encode(clampf(q, -448.f, 448.f));
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t N, int64_t K, void* codes, void* scales,
+                           float* gscale, hipStream_t s) {
+  switch (fmt) {
+    case KF_INT4:
+      k_quant_int4<<<grid_for(N * (K / 128)), kThreads, 0, s>>>(W, N, K, (int8_t*)codes, (uint16_t*)scales);
+      break;
+    case KF_FP8:
+      k_quant_fp8row<<<(unsigned)N, kThreads, 0, s>>>(W, K, (uint8_t*)codes, (float*)scales);
+      break;
+    case KF_NVFP4: {
+      k_fill_f32<<<1, 64, 0, s>>>(gscale, 0.f, 1);
+      const int64_t n = N * K;
+      unsigned g = grid_for(n, kThreads * 16);
+      if (g > 4096) g = 4096;
+      k_absmax_bf16<<<g, kThreads, 0, s>>>(W, n, gscale);
+      k_quant_nvfp4<<<grid_for(N * (K / 16)), kThreads, 0, s>>>(W, N, K, gscale, (uint8_t*)codes,
+                                                                  (uint8_t*)scales);
+      k_nvfp4_global<<<1, 64, 0, s>>>(gscale);
+      break;
+    }
+    case KF_MXFP4:
+      k_quant_mxfp4<<<grid_for(N * (K / 32)), kThreads, 0, s>>>(W, N, K, (uint8_t*)codes, (uint8_t*)scales);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(int fmt, const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s) {
+  if (fmt == KF_FP8) {
+    const int64_t n16 = N * K / 16;
+    k_copy16<<<grid_for(n16), kThreads, 0, s>>>((const u32x4*)codes, n16, (u32x4*)packed);
+  } else {
+    const int64_t n16 = N * K / 32;
+    k_pack4<<<grid_for(n16), kThreads, 0, s>>>(codes, n16, packed);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(int fmt, const void* packed, const void* scales, const float* gscale, int64_t N,
+                             int64_t K, uint16_t* out, hipStream_t s) {
+  const unsigned g = grid_for(N * (K / 8));
+  const uint8_t* P = (const uint8_t*)packed;
+  switch (fmt) {
+    case KF_BF16: {
+      const int64_t n16 = N * K / 8;
+      k_copy16<<<grid_for(n16), kThreads, 0, s>>>((const u32x4*)packed, n16, (u32x4*)out);
+      break;
+    }
+    case KF_INT4: k_dequant<KF_INT4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_FP8: k_dequant<KF_FP8><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_NVFP4: k_dequant<KF_NVFP4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_MXFP4: k_dequant<KF_MXFP4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax(const uint16_t* X, int64_t numel, float* amax, hipStream_t s) {
+  unsigned g = grid_for(numel, kThreads * 16);
+  if (g > 4096) g = 4096;
+  k_absmax_bf16<<<g, kThreads, 0, s>>>(X, numel, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_scale(const float* amax, float* scale, int64_t count, hipStream_t s) {
+  k_fp8_scale<<<grid_for(count, 64), 64, 0, s>>>(amax, scale, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_act(const uint16_t* X, int64_t numel, const float* act_scale, uint8_t* Xq,
+                               hipStream_t s) {
+  k_quant_act<<<grid_for(numel / 8 + 1), kThreads, 0, s>>>(X, numel, act_scale, Xq);
+  return hipGetLastError();
+}
+
+}  // namespace wq
