@@ -138,10 +138,9 @@ wq_status wq_dequantize(int fmt, const void* packed, const void* scales, const f
                         int64_t N, int64_t K, void* W_out, void* stream);
 
 /*
- * Workspace bytes wq_linear / wq_fp8_static_linear need for (M, N, K); 0 means
- * none.  The workspace must be zero-filled before its first use; every call
- * returns the counters it uses to zero before the call's last kernel ends, so
- * the same buffer serves later calls in stream order.  Calls that may run
+ * Workspace bytes wq_linear needs for (M, N, K); 0 means none.  It holds
+ * fp32 split-K partial sums when the launch plan splits K across workgroups
+ * (small problems); no initialisation is needed.  Calls that may run
  * concurrently (different streams) need different workspaces.
  */
 size_t wq_linear_workspace(int fmt, int64_t M, int64_t N, int64_t K);

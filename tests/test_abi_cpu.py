@@ -78,11 +78,11 @@ def test_linear_host_validation():
     # M = 0 and N = 0 are empty calls (nothing launched)
     assert _call_linear(M=0) == wq.OK
     assert _call_linear(N=0) == wq.OK
-    # split-K needs a workspace: 4096x3072 at M=32 plans several K splits
-    need = wq.wq_linear_workspace("int4", 32, 4096, 3072)
+    # split-K needs a workspace: a narrow layer (256 columns) splits K
+    need = wq.wq_linear_workspace("int4", 32, 256, 3072)
     assert need > 0
-    assert _call_linear(M=32, K=3072, N=4096, ws=None) == wq.EWORKSPACE
-    assert _call_linear(M=32, K=3072, N=4096, ws=64, wsb=need - 1) == wq.EWORKSPACE
+    assert _call_linear(M=32, K=3072, N=256, ws=None) == wq.EWORKSPACE
+    assert _call_linear(M=32, K=3072, N=256, ws=64, wsb=need - 1) == wq.EWORKSPACE
     assert b"workspace" in wq.lib().wq_last_error()
 
 
@@ -116,5 +116,6 @@ def test_workspace_plans_are_consistent():
     M, N, K = 32, 4096, 3072
     gemm = wq.wq_linear_workspace("fp8", M, N, K)
     assert wq.wq_fp8_static_workspace(M, N, K) >= gemm + M * K
-    # large M has enough workgroups without K splits
+    # wide layers have enough workgroups without K splits
     assert wq.wq_linear_workspace("mxfp4", 4096, 4096, 3072) == 0
+    assert wq.wq_linear_workspace("int4", 32, 4096, 3072) == 0

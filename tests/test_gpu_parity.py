@@ -150,10 +150,9 @@ def test_linear_no_bias(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_linear_full_size_m32(fmt):
     """The benchmark workload: nn.Linear(3072, 4096), bf16, bias, M=32, in the
-    launch configuration the benchmark times (split-K across workgroups)."""
+    launch configuration the benchmark times."""
     cfg = synth.WORKLOADS[fmt]["cfg"]
     W, b, X = synth.linear_case(4096, 3072, 32, cfg=cfg)
-    assert wq.wq_linear_workspace(fmt, 32, 4096, 3072) > 0  # the split-K path
     q, Y = run_linear(fmt, W, b, X)
     check_quant_exact(fmt, W, q)
     assert_close(Y, oracle_linear(fmt, W, b, X), f"{fmt} 4096x3072 M=32")
@@ -282,3 +281,13 @@ def test_static_large_layer(M):
     rows = np.arange(M) if M <= 64 else np.arange(0, M, 61)
     ref = S.static_linear_fp64(S.quantize_act(X[rows], s_ref), s_ref, wq_ref, ws_ref)
     assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"static 3072->4096 M={M}")
+
+
+def test_workspace_reuse_across_plans():
+    """Calls with different launch plans (K split across workgroups or not)
+    share one cached workspace and run back to back."""
+    cases = [(32, 4096, 3072), (64, 256, 1024), (16, 1024, 2048), (64, 256, 1024), (32, 4096, 3072)]
+    for i, (M, N, K) in enumerate(cases):
+        W, b, X = synth.linear_case(N, K, M, cfg=60 + i)
+        _, Y = run_linear("int4", W, b, X)
+        assert_close(Y, oracle_linear("int4", W, b, X), f"reuse {i} M={M} N={N} K={K}")

@@ -68,6 +68,7 @@ int kernel_k_multiple(int f) {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -178,6 +179,13 @@ static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int6
   if (K % kernel_k_multiple(fmt))
     return fail(WQ_EUNSUPPORTED, "%s linear kernels need K %% %d == 0 (K=%lld)", fmt_name(fmt),
                 kernel_k_multiple(fmt), (long long)K);
+  {
+    // the kernels address X and the packed weight with 32-bit buffer offsets
+    const int64_t wbytes = fmt == WQ_BF16 ? 2 * N * K : (fmt == WQ_FP8 ? N * K : N * K / 2);
+    const int64_t xbytes = kfmt == wq::KF_FP8S ? M * K : 2 * M * K;
+    if (wbytes >= kMaxBufferBytes || xbytes >= kMaxBufferBytes)
+      return fail(WQ_EUNSUPPORTED, "weight or activation buffer of 2^31 bytes or more");
+  }
   if (!X || !W || !Y) return fail(WQ_EINVAL, "null X, weight or Y");
   if (fmt != WQ_BF16 && !scales) return fail(WQ_EINVAL, "null scales");
   if (kfmt == wq::KF_NVFP4 && !gscale) return fail(WQ_EINVAL, "NVFP4 needs global_scale");
@@ -199,7 +207,6 @@ static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int6
   a.bias = (const uint16_t*)bias;
   a.Y = (uint16_t*)Y;
   a.part = p.ws_bytes ? (float*)ws : nullptr;
-  a.cnt = p.ws_bytes ? (unsigned*)((char*)ws + p.part_bytes) : nullptr;
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
@@ -239,9 +246,14 @@ wq_status wq_fp8_quantize_act(const void* X, int64_t M, int64_t K, const float* 
                     "wq_fp8_quantize_act launch");
 }
 
+// Static-FP8 workspace: [split-K partials][quantized X].
+static size_t static_xq_offset(int64_t M, int64_t N, int64_t K) {
+  return align256(wq::plan_linear(wq::KF_FP8S, M, N, K).part_bytes);
+}
+
 size_t wq_fp8_static_workspace(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return align256((size_t)M * (size_t)K) + wq::plan_linear(wq::KF_FP8S, M, N, K).ws_bytes;
+  return static_xq_offset(M, N, K) + align256((size_t)M * (size_t)K);
 }
 
 wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float* act_scale, const void* Wq,
@@ -259,11 +271,11 @@ wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float*
   if (!X || !act_scale || !Wq || !w_scale || !Y) return fail(WQ_EINVAL, "wq_fp8_static_linear: null pointer");
   if (!aligned16(X) || !aligned16(Wq) || !aligned16(Y))
     return fail(WQ_EALIGN, "X, Wq and Y must be 16-byte aligned");
-  const size_t xq_bytes = align256((size_t)M * (size_t)K);
-  wq_status st = wq_fp8_quantize_act(X, M, K, act_scale, workspace, stream);
+  void* xq = (char*)workspace + static_xq_offset(M, N, K);
+  wq_status st = wq_fp8_quantize_act(X, M, K, act_scale, xq, stream);
   if (st != WQ_OK) return st;
-  return linear_common(wq::KF_FP8S, WQ_FP8, workspace, M, K, Wq, w_scale, nullptr, act_scale, bias, N, Y,
-                       (char*)workspace + xq_bytes, workspace_bytes - xq_bytes, stream);
+  return linear_common(wq::KF_FP8S, WQ_FP8, xq, M, K, Wq, w_scale, nullptr, act_scale, bias, N, Y, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -12,14 +12,27 @@ namespace wq {
 // variant used by the static path).
 enum KFmt { KF_BF16 = 0, KF_INT4 = 1, KF_FP8 = 2, KF_NVFP4 = 3, KF_MXFP4 = 4, KF_FP8S = 5 };
 
+// Workspace: split-K partial sums (fp32) when a plan splits K across
+// workgroups; the static path appends its quantized activations.
+constexpr int kMaxSplit = 8;  // K splits across workgroups of one column tile
+
 // Launch plan of the small-M dequant-GEMM (shared by the workspace query and
 // the launch so both always agree).
+// Tile configurations of the small-M kernel:
+//  kCfgSplit   : 64 columns x 4 waves per workgroup, K split across workgroups
+//  kCfgNoSplit : 16 columns x 12 waves per workgroup covering all of K
+constexpr int kCfgSplit = 0;
+constexpr int kCfgNoSplit = 1;
+
 struct LinearPlan {
+  int cfg;        // kCfgSplit or kCfgNoSplit
   int mt;         // 16-row MFMA tiles per workgroup (1, 2 or 4)
-  int gx, gz;     // workgroups along N (64 columns each) and along M
+  int ntw;        // 16-column tiles per wave (= per workgroup)
+  int nwaves;     // waves per workgroup
+  int spw;        // K macro-steps per wave whose loads are issued together
+  int gx, gz;     // workgroups along N and along M
   int S;          // K splits across workgroups
-  int spw;        // K macro-steps per wave
-  size_t part_bytes, cnt_bytes, ws_bytes;
+  size_t part_bytes, ws_bytes;  // split-K partials (0 without a split)
 };
 
 LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K);
@@ -33,7 +46,6 @@ struct LinearArgs {
   const uint16_t* bias;  // bf16 [N] or null
   uint16_t* Y;           // bf16 [M][N]
   float* part;           // split-K partials (workspace)
-  unsigned* cnt;         // split-K arrival counters (workspace, zero between calls)
   int M, N, K;
 };
 

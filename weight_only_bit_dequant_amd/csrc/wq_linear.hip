@@ -143,237 +143,348 @@ __device__ __forceinline__ f32x4 mfma_fp8(uint32_t a0, uint32_t a1, uint32_t b0,
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
 
-template <int F>
-__device__ __forceinline__ float column_scale(const LinearArgs& a, int n) {
-  if constexpr (F == KF_FP8) return reinterpret_cast<const float*>(a.scales)[n];
-  else if constexpr (F == KF_NVFP4) return a.gscale[0];
-  else return 1.0f;
+// Buffer loads: an offset at or beyond the resource size reads as zero, which
+// masks the M, N and K tails without branches (a branch per masked load makes
+// the compiler wait for every outstanding load at each join).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
-template <int F, int MT>
-__global__ __launch_bounds__(256) void k_linear_small(LinearArgs a, int S, int spw) {
+constexpr uint32_t kOOB = 0x80000000u;  // beyond every resource (sizes are < 2^31)
+
+// Output epilogue: y = acc * column scale (+ bias) -> bf16 (nearest even).
+// Column scale: FP8 row scale, NVFP4 global scale, static FP8
+// act_scale * w_scale[n]; 1 otherwise.
+template <int F>
+struct Epilogue {
+  float scale1, scale2, bias;
+  __device__ __forceinline__ Epilogue(const LinearArgs& a, int en, uint32_t bias_bits, uint32_t cs_bits) {
+    bias = bitsf(bias_bits << 16);
+    scale2 = 1.0f;
+    if constexpr (F == KF_FP8) scale1 = bitsf(cs_bits);
+    else if constexpr (F == KF_NVFP4) scale1 = a.gscale[0];
+    else if constexpr (F == KF_FP8S) {
+      scale1 = a.act_scale[0];
+      scale2 = bitsf(cs_bits);
+    } else scale1 = 1.0f;
+  }
+  __device__ __forceinline__ void store(const LinearArgs& a, int m0, int en, int e, int E, int NT, float v) const {
+    const int m = m0 + e / NT;
+    if (e < E && m < a.M && en < a.N) {
+      float y = v * scale1;
+      if constexpr (F == KF_FP8S) y = y * scale2;
+      a.Y[(int64_t)m * a.N + en] = f32_to_bf16(y + bias);
+    }
+  }
+};
+
+// K-split plan of one workgroup: NW waves x SPW macro-steps each per block;
+// the S workgroups of a column tile interleave their blocks.
+//
+// Template parameters: F format, MT 16-row tiles, NTW 16-column tiles per wave,
+// NW waves per workgroup, SPW macro-steps whose loads are issued together.
+template <int F, int MT, int NTW, int NW, int SPW>
+__global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   constexpr int KPL = FmtT<F>::KPL;
   constexpr int MACRO = 4 * KPL;
   constexpr bool ACT8 = (F == KF_FP8S);
-  constexpr int XL = ACT8 ? 1 : KPL / 8;  // 16-byte activation loads per m-tile
-  constexpr int E = MT * 16 * 64;         // outputs of the workgroup tile
-  __shared__ float red[3 * E];
-  __shared__ int last_flag;
+  constexpr int XL = ACT8 ? 1 : KPL / 8;  // 16-byte activation loads per m-tile per step
+  constexpr int NT = 16 * NTW;            // columns per workgroup
+  constexpr int E = MT * 16 * NT;         // outputs per workgroup
+  constexpr int NTHR = NW * 64;
+  __shared__ float red[(NW - 1) * E];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int n0 = blockIdx.x * 64;
+  const int n0 = blockIdx.x * NT;
   const int split = blockIdx.y;
   const int m0 = blockIdx.z * (16 * MT);
   const int M = a.M, N = a.N, K = a.K;
   const int T = (K + MACRO - 1) / MACRO;
-  const int t0 = (split * 4 + wave) * spw;
-  const int t1 = min(t0 + spw, T);
+  const uint32_t wrow = (uint32_t)kbyte<F>(K);
 
-  const uint8_t* __restrict__ Wb = reinterpret_cast<const uint8_t*>(a.W);
-  const int64_t wrow = kbyte<F>(K);
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * wrow);
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * (uint32_t)K * (ACT8 ? 1u : 2u));
+  uint32_t sbytes = 0;
+  if constexpr (F == KF_INT4) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 2u;
+  else if constexpr (F == KF_NVFP4) sbytes = (uint32_t)N * (uint32_t)(K / 16);
+  else if constexpr (F == KF_MXFP4) sbytes = (uint32_t)N * (uint32_t)(K / 32);
+  else if constexpr (F == KF_FP8 || F == KF_FP8S) sbytes = (uint32_t)N * 4u;
+  const __amdgpu_buffer_rsrc_t Sr = make_rsrc(a.scales ? a.scales : a.W, a.scales ? sbytes : 0u);
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
 
-  f32x4 acc[MT][4];
+  // epilogue operands of this thread's column, fetched early so they travel
+  // with the main loads
+  const int ecol = tid % NT;
+  const int en = n0 + ecol;
+  const uint32_t bias_bits = bload16(Br, (uint32_t)en * 2u);
+  uint32_t cs_bits = 0x3F800000u;  // 1.0f
+  if constexpr (F == KF_FP8 || F == KF_FP8S) cs_bits = bload32(Sr, (uint32_t)en * 4u);
+
+  f32x4 acc[MT][NTW];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ts = t0; ts < t1; ++ts) {
-    const int kl = ts * MACRO + g * KPL;
-    const bool kv = kl < K;
-    u32x4 w[4];
+  const int wi = split * NW + wave;
+  for (int blk = wi; blk * SPW < T; blk += S * NW) {
+    // ---- issue every load of this block before any wait
+    u32x4 w[SPW][NTW];
+    u32x4 xv[SPW][MT][XL];
+    uint32_t sc[SPW][NTW];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = n0 + 16 * t + c;
-      w[t] = (kv && n < N) ? *reinterpret_cast<const u32x4*>(Wb + (int64_t)n * wrow + kbyte<F>(kl))
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
-    u32x4 xv[MT][XL];
+    for (int st = 0; st < SPW; ++st) {
+      const int kl = (blk * SPW + st) * MACRO + g * KPL;
+      const bool kv = kl < K;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int m = m0 + 16 * i + c;
-      const bool ok = kv && m < M;
-#pragma unroll
-      for (int j = 0; j < XL; ++j) {
-        if constexpr (ACT8)
-          xv[i][j] = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.X) + (int64_t)m * K + kl)
-                        : u32x4{0u, 0u, 0u, 0u};
-        else
-          xv[i][j] = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.X) + (int64_t)m * K +
-                                                          kl + 8 * j)
-                        : u32x4{0u, 0u, 0u, 0u};
+      for (int t = 0; t < NTW; ++t) {
+        const uint32_t n = (uint32_t)(n0 + 16 * t + c);
+        w[st][t] = bload128(Wr, kv ? n * wrow + (uint32_t)kbyte<F>(kl) : kOOB);
+        if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, kv ? (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u : kOOB);
+        else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, kv ? n * (uint32_t)(K / 16) + (uint32_t)(kl / 16) : kOOB);
+        else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, kv ? n * (uint32_t)(K / 32) + (uint32_t)(kl / 32) : kOOB);
+        else sc[st][t] = 0u;
       }
-    }
-
-    if constexpr (F == KF_INT4) {
-      float sc[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = n0 + 16 * t + c;
-        sc[t] = (kv && n < N)
-                    ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.scales)[(int64_t)n * (K / 128) + kl / 128])
-                    : 0.f;
-      }
-      f32x4 tmp[MT][4], rs[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        rs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t m = (uint32_t)(m0 + 16 * i + c);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) tmp[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 b[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = dec_int4_biased(w[t][j]);
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const bf16x8 A = as_bf16x8(xv[i][j]);
-          rs[i] = mfma_bf16(A, ones, rs[i]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) tmp[i][t] = mfma_bf16(A, b[t], tmp[i][t]);
+        for (int j = 0; j < XL; ++j) {
+          if constexpr (ACT8) xv[st][i][j] = bload128(Xr, kv ? m * (uint32_t)K + (uint32_t)kl : kOOB);
+          else xv[st][i][j] = bload128(Xr, kv ? (m * (uint32_t)K + (uint32_t)kl + 8u * j) * 2u : kOOB);
         }
       }
+    }
+
+    // ---- decode and multiply
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+    for (int st = 0; st < SPW; ++st) {
+      if constexpr (F == KF_INT4) {
+        f32x4 tmp[MT][NTW], rs[MT];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < MT; ++i) {
+          rs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(sc[t], fmaf(-136.f, rs[i][r], tmp[i][t][r]), acc[i][t][r]);
-    } else if constexpr (F == KF_NVFP4) {
-      float d0[4], d1[4];
+          for (int t = 0; t < NTW; ++t) tmp[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = n0 + 16 * t + c;
-        const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.scales) + (int64_t)n * (K / 16) + kl / 16;
-        const bool ok = kv && n < N;
-        d0[t] = ok ? e4m3_decode(sp[0]) : 0.f;
-        d1[t] = ok ? e4m3_decode(sp[1]) : 0.f;
-      }
+        for (int j = 0; j < 4; ++j) {
+          bf16x8 b[NTW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 b[4];
+          for (int t = 0; t < NTW; ++t) b[t] = dec_int4_biased(w[st][t][j]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = dec_fp4_mul(w[t][j], j < 2 ? d0[t] : d1[t]);
+          for (int i = 0; i < MT; ++i) {
+            const bf16x8 A = as_bf16x8(xv[st][i][j]);
+            rs[i] = mfma_bf16(A, ones, rs[i]);
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) tmp[i][t] = mfma_bf16(A, b[t], tmp[i][t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const float s = bitsf(sc[st][t] << 16);
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(s, fmaf(-136.f, rs[i][r], tmp[i][t][r]), acc[i][t][r]);
+        }
+      } else if constexpr (F == KF_NVFP4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8 b[NTW];
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) b[t] = dec_fp4_mul(w[st][t][j], e4m3_decode((sc[st][t] >> (j < 2 ? 0 : 8)) & 0xFFu));
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) acc[i][t] = mfma_bf16(as_bf16x8(xv[st][i][j]), b[t], acc[i][t]);
+        }
+      } else if constexpr (F == KF_MXFP4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8 b[NTW];
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) b[t] = dec_fp4_pow2(w[st][t][j], e8m0_decode(sc[st][t]));
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) acc[i][t] = mfma_bf16(as_bf16x8(xv[st][i][j]), b[t], acc[i][t]);
+        }
+      } else if constexpr (F == KF_FP8) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          bf16x8 b[NTW];
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) b[t] = dec_fp8(w[st][t][2 * j], w[st][t][2 * j + 1]);
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) acc[i][t] = mfma_bf16(as_bf16x8(xv[st][i][j]), b[t], acc[i][t]);
+        }
+      } else if constexpr (F == KF_BF16) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[i][t] = mfma_bf16(as_bf16x8(xv[i][j]), b[t], acc[i][t]);
+          for (int t = 0; t < NTW; ++t) acc[i][t] = mfma_bf16(as_bf16x8(xv[st][i][0]), as_bf16x8(w[st][t]), acc[i][t]);
+      } else {  // KF_FP8S: E4M3 activations x E4M3 weights
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t)
+              acc[i][t] = mfma_fp8(xv[st][i][0][2 * j], xv[st][i][0][2 * j + 1], w[st][t][2 * j],
+                                   w[st][t][2 * j + 1], acc[i][t]);
       }
-    } else if constexpr (F == KF_MXFP4) {
-      float p[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = n0 + 16 * t + c;
-        p[t] = (kv && n < N) ? e8m0_decode(reinterpret_cast<const uint8_t*>(a.scales)[(int64_t)n * (K / 32) + kl / 32])
-                             : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 b[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = dec_fp4_pow2(w[t][j], p[t]);
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[i][t] = mfma_bf16(as_bf16x8(xv[i][j]), b[t], acc[i][t]);
-      }
-    } else if constexpr (F == KF_FP8) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8 b[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = dec_fp8(w[t][2 * j], w[t][2 * j + 1]);
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[i][t] = mfma_bf16(as_bf16x8(xv[i][j]), b[t], acc[i][t]);
-      }
-    } else if constexpr (F == KF_BF16) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = mfma_bf16(as_bf16x8(xv[i][0]), as_bf16x8(w[t]), acc[i][t]);
-    } else {  // KF_FP8S: E4M3 activations x E4M3 weights
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[i][t] = mfma_fp8(xv[i][0][2 * j], xv[i][0][2 * j + 1], w[t][2 * j], w[t][2 * j + 1], acc[i][t]);
     }
   }
 
-  // ---- reduce the 4 wave partials: waves 1..3 through LDS into wave 0
+  // ---- reduce the wave partials: waves 1.. through LDS into wave 0, which
+  // leaves the workgroup total in the first LDS slice
   if (wave > 0) {
     float* dst = red + (wave - 1) * E;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * 64 + 16 * t + c] = acc[i][t][r];
+        for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * NT + 16 * t + c] = acc[i][t][r];
   }
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < NTW; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int e = (16 * i + 4 * g + r) * 64 + 16 * t + c;
-          red[e] = acc[i][t][r] + red[e] + red[E + e] + red[2 * E + e];
+          const int e = (16 * i + 4 * g + r) * NT + 16 * t + c;
+          float v = acc[i][t][r];
+#pragma unroll
+          for (int w2 = 0; w2 < NW - 1; ++w2) v += red[w2 * E + e];
+          red[e] = v;
         }
   }
   __syncthreads();
 
-  // ---- epilogue (directly, or after the cross-workgroup split-K reduction)
-  auto store = [&](int e, float v) {
-    const int m = m0 + (e >> 6), n = n0 + (e & 63);
-    if (m < M && n < N) {
-      float y;
-      if constexpr (F == KF_FP8S) y = (v * a.act_scale[0]) * reinterpret_cast<const float*>(a.scales)[n];
-      else y = v * column_scale<F>(a, n);
-      if (a.bias) y += bf16_to_f32(a.bias[n]);
-      a.Y[(int64_t)m * N + n] = f32_to_bf16(y);
-    }
-  };
-
+  // ---- epilogue: column scale, bias, one rounding to bf16.  Thread tid owns
+  // the outputs e = tid + q * NTHR (q < EPT), all in column n0 + tid % NT.
+  constexpr int EPT = (E + NTHR - 1) / NTHR;
+  float v[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int e = tid + q * NTHR;
+    v[q] = (e < E) ? red[e] : 0.f;
+  }
   if (S == 1) {
-    for (int e = tid; e < E; e += 256) store(e, red[e]);
+    const Epilogue<F> ep(a, en, bias_bits, cs_bits);
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) ep.store(a, m0, en, tid + q * NTHR, E, NT, v[q]);
     return;
   }
+  // ---- split-K: publish this workgroup's partial (thread-major, 16-byte
+  // vectors); k_splitk_reduce, launched next on the same stream, sums the S
+  // partials of each tile in a fixed order.  Stream order makes the partials
+  // visible to it without any device-wide fence here.
+  constexpr int V4 = (EPT + 3) / 4;
   const int tile = blockIdx.z * gridDim.x + blockIdx.x;
-  float* mine = a.part + ((int64_t)tile * S + split) * E;
-  for (int e = tid; e < E; e += 256) mine[e] = red[e];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last_flag = (atomicAdd(&a.cnt[tile], 1u) == (unsigned)(S - 1));
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  const float* base = a.part + (int64_t)tile * S * E;
-  for (int e = tid; e < E; e += 256) {
-    float v = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) v += base[(int64_t)s2 * E + e];
-    store(e, v);
+  float* mine = a.part + ((int64_t)tile * S + split) * (NTHR * V4 * 4);
+#pragma unroll
+  for (int q4 = 0; q4 < V4; ++q4) {
+    f32x4 o{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * q4 + r < EPT) o[r] = v[4 * q4 + r];
+    *reinterpret_cast<f32x4*>(mine + (tid * V4 + q4) * 4) = o;
   }
-  if (tid == 0) a.cnt[tile] = 0u;
+}
+
+// Sums the S split-K partials of each column tile (same thread mapping as the
+// producing kernel) and applies the epilogue.  All partial loads of a thread
+// are issued before the first add.
+template <int F, int MT, int NTW, int NW>
+__global__ __launch_bounds__(NW * 64) void k_splitk_reduce(LinearArgs a, int S) {
+  constexpr int NT = 16 * NTW;
+  constexpr int E = MT * 16 * NT;
+  constexpr int NTHR = NW * 64;
+  constexpr int EPT = (E + NTHR - 1) / NTHR;
+  constexpr int V4 = (EPT + 3) / 4;
+  const int tid = threadIdx.x;
+  const int n0 = blockIdx.x * NT, m0 = blockIdx.z * (16 * MT);
+  const int en = n0 + tid % NT;
+  const int N = a.N;
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  const uint32_t bias_bits = bload16(Br, (uint32_t)en * 2u);
+  uint32_t cs_bits = 0x3F800000u;
+  if constexpr (F == KF_FP8 || F == KF_FP8S) {
+    const __amdgpu_buffer_rsrc_t Sr = make_rsrc(a.scales, (uint32_t)N * 4u);
+    cs_bits = bload32(Sr, (uint32_t)en * 4u);
+  }
+  const int tile = blockIdx.z * gridDim.x + blockIdx.x;
+  const uint32_t slab = (uint32_t)(NTHR * V4 * 16);
+  const __amdgpu_buffer_rsrc_t Pr = make_rsrc(a.part + (int64_t)tile * S * (NTHR * V4 * 4), (uint32_t)S * slab);
+  u32x4 pv[kMaxSplit][V4];
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSplit; ++s2)
+#pragma unroll
+    for (int q4 = 0; q4 < V4; ++q4) pv[s2][q4] = bload128(Pr, (uint32_t)s2 * slab + (uint32_t)(tid * V4 + q4) * 16u);
+  float v[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) v[q] = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSplit; ++s2)
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) v[q] += bitsf(pv[s2][q / 4][q % 4]);
+  const Epilogue<F> ep(a, en, bias_bits, cs_bits);
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) ep.store(a, m0, en, tid + q * NTHR, E, NT, v[q]);
+}
+
+// Steps per wave whose loads are issued together: one 16-byte weight chunk
+// per tile and step, sized so that a no-split workgroup of 12 waves covers a
+// 3072-deep K in one pass.
+template <int F>
+constexpr int spw_nosplit() {
+  return (F == KF_BF16) ? 8 : ((F == KF_FP8 || F == KF_FP8S) ? 4 : 2);
+}
+template <int F>
+constexpr int spw_split() {
+  return (F == KF_BF16) ? 4 : ((F == KF_FP8 || F == KF_FP8S) ? 2 : 1);
+}
+
+template <int F, int MT>
+hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  dim3 grid(p.gx, p.S, p.gz);
+  if (p.cfg == kCfgSplit) {
+    k_linear<F, MT, 4, 4, spw_split<F>()><<<grid, 256, 0, s>>>(a, p.S);
+    if (p.S > 1) k_splitk_reduce<F, MT, 4, 4><<<dim3(p.gx, 1, p.gz), 256, 0, s>>>(a, p.S);
+  } else {
+    k_linear<F, MT, 1, 12, spw_nosplit<F>()><<<grid, 768, 0, s>>>(a, p.S);
+  }
+  return hipGetLastError();
 }
 
 template <int F>
 hipError_t launch_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  dim3 grid(p.gx, p.S, p.gz);
   switch (p.mt) {
-    case 1: k_linear_small<F, 1><<<grid, 256, 0, s>>>(a, p.S, p.spw); break;
-    case 2: k_linear_small<F, 2><<<grid, 256, 0, s>>>(a, p.S, p.spw); break;
-    default: k_linear_small<F, 4><<<grid, 256, 0, s>>>(a, p.S, p.spw); break;
+    case 1: return launch_mt<F, 1>(a, p, s);
+    case 2: return launch_mt<F, 2>(a, p, s);
+    default: return launch_mt<F, 4>(a, p, s);
   }
-  return hipGetLastError();
 }
 
 int kpl_of(int kfmt) {
@@ -385,35 +496,45 @@ int kpl_of(int kfmt) {
   }
 }
 
+int spw_of(int kfmt, int cfg) {
+  const bool b16 = kfmt == KF_BF16, f8 = (kfmt == KF_FP8 || kfmt == KF_FP8S);
+  if (cfg == kCfgSplit) return b16 ? 4 : (f8 ? 2 : 1);
+  return b16 ? 8 : (f8 ? 4 : 2);
+}
+
 }  // namespace
 
 LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
   LinearPlan p{};
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.gz = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
-  p.gx = (int)((N + 63) / 64);
-  const int64_t macro = 4 * kpl_of(kfmt);
-  const int64_t T = (K + macro - 1) / macro;
-  int spw = (kfmt == KF_BF16) ? 4 : ((kfmt == KF_FP8 || kfmt == KF_FP8S) ? 2 : 1);
-  int64_t S = (T + 4 * spw - 1) / (4 * spw);
+  // No-split (16 columns x all of K per workgroup) whenever it yields enough
+  // workgroups to cover the chip; otherwise 64-column tiles with K split
+  // across workgroups and a second, stream-ordered reduction kernel.
+  const int64_t gx_nosplit = (N + 15) / 16;
+  p.cfg = (gx_nosplit * p.gz >= 128) ? kCfgNoSplit : kCfgSplit;
+  const int64_t T = (K + 4 * kpl_of(kfmt) - 1) / (4 * kpl_of(kfmt));
+  if (p.cfg == kCfgSplit) {
+    p.ntw = 4;
+    p.nwaves = 4;
+  } else {
+    p.ntw = 1;
+    p.nwaves = 12;
+  }
+  p.spw = spw_of(kfmt, p.cfg);
+  p.gx = (int)((N + 16 * p.ntw - 1) / (16 * p.ntw));
   const int64_t base = (int64_t)p.gx * p.gz;
-  if (base >= 256) S = 1;
-  if (S < 1) S = 1;
-  spw = (int)((T + 4 * S - 1) / (4 * S));
-  if (spw < 1) spw = 1;
-  S = (T + 4 * spw - 1) / (4 * spw);
+  int64_t S = 1;
+  if (p.cfg == kCfgSplit) S = (T + (int64_t)p.nwaves * p.spw - 1) / ((int64_t)p.nwaves * p.spw);
+  if (S > kMaxSplit) S = kMaxSplit;  // the waves then loop over several blocks
   if (S < 1) S = 1;
   p.S = (int)S;
-  p.spw = spw;
-  const int64_t E = (int64_t)p.mt * 16 * 64;
-  if (p.S > 1) {
-    p.part_bytes = (size_t)(base * p.S * E * 4);
-    p.cnt_bytes = (size_t)(((base * 4) + 255) / 256 * 256);
-  } else {
-    p.part_bytes = 0;
-    p.cnt_bytes = 0;
-  }
-  p.ws_bytes = p.part_bytes + p.cnt_bytes;
+  const int64_t E = (int64_t)p.mt * 16 * 16 * p.ntw;
+  const int64_t nthr = 64 * (int64_t)p.nwaves;
+  const int64_t ept = (E + nthr - 1) / nthr;
+  const int64_t slab = nthr * ((ept + 3) / 4) * 16;  // bytes of one workgroup partial
+  p.part_bytes = p.S > 1 ? (size_t)(base * p.S * slab) : 0;
+  p.ws_bytes = p.part_bytes;
   return p;
 }
 
