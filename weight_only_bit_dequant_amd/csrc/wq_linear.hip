@@ -36,6 +36,8 @@
 //          with a multiply.)
 //  MXFP4 : v_cvt_scalef32_pk_bf16_fp4 with the power-of-two E8M0 scale.
 //  BF16  : the dense weight (the unquantized Linear), no decode.
+#include <atomic>
+
 #include "wq_device.hpp"
 #include "wq_internal.hpp"
 
@@ -195,7 +197,32 @@ struct Epilogue {
 //
 // Template parameters: F format, MT 16-row tiles, NTW 16-column tiles per wave,
 // NW waves per workgroup, SPW macro-steps whose loads are issued together.
-template <int F, int MT, int NTW, int NW, int SPW>
+// Activation staging through LDS (XLDS): the MFMA operand layout wants lane
+// (g, c) to hold row c, K-chunk g, so loading it straight from a row-major X
+// touches 16 rows per load instruction.  With XLDS each wave instead loads
+// its [16*MT rows x one K macro-step] slice with contiguous 16-byte loads
+// (L lanes per row, R rows per instruction), writes it into a private padded
+// LDS slot and reads it back in the operand layout.
+template <int F, int MT>
+struct XStage {
+  static constexpr int KPL = FmtT<F>::KPL;
+  static constexpr int MACRO = 4 * KPL;
+  static constexpr int XB = (F == KF_FP8S) ? 1 : 2;  // bytes per activation element
+  static constexpr int ROWB = MACRO * XB + 16;        // padded LDS row
+  static constexpr int SLOT = 16 * MT * ROWB;         // one wave's slice
+  static constexpr int L = MACRO * XB / 16;           // lanes per row
+  static constexpr int R = 64 / L;                    // rows per load instruction
+};
+
+template <int F, int MT, int NTW, int NW>
+constexpr int smem_bytes(bool xlds) {
+  const int E = MT * 16 * 16 * NTW;
+  const int red = (NW - 1) * E * 4;
+  const int xs = xlds ? NW * XStage<F, MT>::SLOT : 0;
+  return (red > xs ? red : xs) > 16 ? (red > xs ? red : xs) : 16;
+}
+
+template <int F, int MT, int NTW, int NW, int SPW, bool XLDS>
 __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   constexpr int KPL = FmtT<F>::KPL;
   constexpr int MACRO = 4 * KPL;
@@ -204,7 +231,10 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   constexpr int NT = 16 * NTW;            // columns per workgroup
   constexpr int E = MT * 16 * NT;         // outputs per workgroup
   constexpr int NTHR = NW * 64;
-  __shared__ float red[(NW - 1) * E];
+  using XS = XStage<F, MT>;
+  static_assert(!XLDS || XS::R * MT * XL == 16 * MT, "XLDS: load instructions must cover the slice rows");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float* red = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -263,8 +293,17 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
         const uint32_t m = (uint32_t)(m0 + 16 * i + c);
 #pragma unroll
         for (int j = 0; j < XL; ++j) {
-          if constexpr (ACT8) xv[st][i][j] = bload128(Xr, kv ? m * (uint32_t)K + (uint32_t)kl : kOOB);
-          else xv[st][i][j] = bload128(Xr, kv ? (m * (uint32_t)K + (uint32_t)kl + 8u * j) * 2u : kOOB);
+          if constexpr (XLDS) {
+            // contiguous: instruction q covers rows q*R .. q*R+R-1 of the slice
+            const int q = i * XL + j;
+            const uint32_t row = (uint32_t)(m0 + q * XS::R + lane / XS::L);
+            const int kx = (blk * SPW + st) * MACRO + (lane % XS::L) * (16 / XS::XB);
+            xv[st][i][j] = bload128(Xr, kx < K ? (row * (uint32_t)K + (uint32_t)kx) * (uint32_t)XS::XB : kOOB);
+          } else if constexpr (ACT8) {
+            xv[st][i][j] = bload128(Xr, kv ? m * (uint32_t)K + (uint32_t)kl : kOOB);
+          } else {
+            xv[st][i][j] = bload128(Xr, kv ? (m * (uint32_t)K + (uint32_t)kl + 8u * j) * 2u : kOOB);
+          }
         }
       }
     }
@@ -272,6 +311,23 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     // ---- decode and multiply
 #pragma unroll
     for (int st = 0; st < SPW; ++st) {
+      if constexpr (XLDS) {
+        // through this wave's LDS slot into the operand layout (a wave's LDS
+        // operations execute in order, so no barrier is needed here)
+        unsigned char* slot = smem + wave * XS::SLOT;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < XL; ++j) {
+            const int q = i * XL + j;
+            *reinterpret_cast<u32x4*>(slot + (q * XS::R + lane / XS::L) * XS::ROWB + (lane % XS::L) * 16) = xv[st][i][j];
+          }
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < XL; ++j)
+            xv[st][i][j] = *reinterpret_cast<const u32x4*>(slot + (16 * i + c) * XS::ROWB + (g * KPL + 8 * j) * XS::XB);
+      }
       if constexpr (F == KF_INT4) {
         f32x4 tmp[MT][NTW], rs[MT];
 #pragma unroll
@@ -355,6 +411,7 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
 
   // ---- reduce the wave partials: waves 1.. through LDS into wave 0, which
   // leaves the workgroup total in the first LDS slice
+  if constexpr (XLDS) __syncthreads();  // the activation slots are reused
   if (wave > 0) {
     float* dst = red + (wave - 1) * E;
 #pragma unroll
@@ -466,14 +523,33 @@ constexpr int spw_split() {
   return (F == KF_BF16) ? 4 : ((F == KF_FP8 || F == KF_FP8S) ? 2 : 1);
 }
 
+// Dynamic LDS above 64 KiB must be allowed per kernel once per process.
+template <typename Kern>
+hipError_t allow_smem(Kern k, int bytes, std::atomic<int>& done) {
+  if (bytes <= 65536 || done.load(std::memory_order_acquire)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.store(1, std::memory_order_release);
+  return e;
+}
+
 template <int F, int MT>
 hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   dim3 grid(p.gx, p.S, p.gz);
   if (p.cfg == kCfgSplit) {
-    k_linear<F, MT, 4, 4, spw_split<F>()><<<grid, 256, 0, s>>>(a, p.S);
+    constexpr int sm = smem_bytes<F, MT, 4, 4>(false);
+    k_linear<F, MT, 4, 4, spw_split<F>(), false><<<grid, 256, sm, s>>>(a, p.S);
     if (p.S > 1) k_splitk_reduce<F, MT, 4, 4><<<dim3(p.gx, 1, p.gz), 256, 0, s>>>(a, p.S);
+  } else if constexpr (MT <= 2) {
+    // no-split tiles with activations staged through LDS
+    constexpr int sm = smem_bytes<F, MT, 1, 12>(true);
+    static std::atomic<int> done{0};
+    auto k = k_linear<F, MT, 1, 12, spw_nosplit<F>(), true>;
+    hipError_t e = allow_smem(k, sm, done);
+    if (e != hipSuccess) return e;
+    k<<<grid, 768, sm, s>>>(a, p.S);
   } else {
-    k_linear<F, MT, 1, 12, spw_nosplit<F>()><<<grid, 768, 0, s>>>(a, p.S);
+    constexpr int sm = smem_bytes<F, MT, 1, 12>(false);
+    k_linear<F, MT, 1, 12, spw_nosplit<F>(), false><<<grid, 768, sm, s>>>(a, p.S);
   }
   return hipGetLastError();
 }
