@@ -1,0 +1,282 @@
+// Tiled dequant-GEMM for larger M, where the contraction (2*M*N*K FLOP)
+// rather than the weight stream bounds the time.
+//
+// One workgroup (4 waves, 2 x 2) computes a BM x BN output tile.  K advances in
+// steps of 64.  Per step:
+//  * every thread loads its share of the activation tile (contiguous 16-byte
+//    loads) and of the packed weight tile for the NEXT step, so global
+//    latency overlaps the current step's matrix-core work;
+//  * the weight chunk is decoded once per workgroup into bf16 (E4M3 for the
+//    static path) and written to LDS next to the activation tile (double
+//    buffered, rows padded by 16 bytes so the operand reads hit distinct
+//    banks);
+//  * each wave reads 16x32 operand fragments from LDS and issues
+//    v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x32_fp8_fp8 for static FP8).
+// Decode: FP8 weights, NVFP4 (E2M1 x E4M3 block scale) and MXFP4 (E2M1 x
+// 2^e) are exact in bf16; the FP8 row scale, the NVFP4 global scale and the
+// static activation x weight scales go to the epilogue.  INT4 is decoded as
+// bf16(code * s), the dequantized weight of the two-kernel form (at most one
+// bf16 rounding per weight).  Workgroups are mapped to tiles so that the
+// tiles resident on one XCD share activation rows in that XCD's L2.
+#include "wq_kernel_common.hpp"
+
+namespace wq {
+
+namespace {
+
+constexpr int kBK = 64;  // K elements per step
+
+template <int F>
+struct TileFmt {
+  static constexpr bool ACT8 = (F == KF_FP8S);
+  static constexpr int XB = ACT8 ? 1 : 2;  // bytes per activation element in LDS
+  static constexpr int OB = ACT8 ? 1 : 2;  // bytes per weight operand element in LDS
+  // packed weight bytes per column per step
+  static constexpr int WSTEP = (F == KF_BF16) ? 128 : ((F == KF_FP8 || F == KF_FP8S) ? 64 : 32);
+  static constexpr int ARS = kBK * XB + 16;  // padded LDS row strides
+  static constexpr int BRS = kBK * OB + 16;
+};
+
+template <int F, int BM, int BN>
+constexpr int tile_smem() {
+  return 2 * (BM * TileFmt<F>::ARS + BN * TileFmt<F>::BRS);
+}
+
+// Decode one 16-byte packed chunk of a weight column into operand bytes in
+// LDS (`sc` holds the chunk's scale codes).
+template <int F>
+__device__ __forceinline__ void decode_store(unsigned char* dst, u32x4 w, uint32_t sc) {
+  if constexpr (F == KF_INT4) {
+    const float s = bitsf(sc << 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // 8 nibbles -> bf16(code * s), K order kept
+      const bf16x8 biased = dec_int4_biased(w[j]);  // 136 + code, exact
+      const u32x4 bb = __builtin_bit_cast(u32x4, biased);
+      bf16x8 r;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float lo = bitsf(bb[p] << 16), hi = bitsf(bb[p] & 0xFFFF0000u);
+        r[2 * p] = (__bf16)fmaf(lo, s, -136.f * s);
+        r[2 * p + 1] = (__bf16)fmaf(hi, s, -136.f * s);
+      }
+      *reinterpret_cast<bf16x8*>(dst + 16 * j) = r;
+    }
+  } else if constexpr (F == KF_NVFP4) {
+    const float d0 = e4m3_decode(sc & 0xFFu), d1 = e4m3_decode((sc >> 8) & 0xFFu);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(dst + 16 * j) = dec_fp4_mul(w[j], j < 2 ? d0 : d1);
+  } else if constexpr (F == KF_MXFP4) {
+    const float p = e8m0_decode(sc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(dst + 16 * j) = dec_fp4_pow2(w[j], p);
+  } else if constexpr (F == KF_FP8) {
+    *reinterpret_cast<bf16x8*>(dst) = dec_fp8(w[0], w[1]);
+    *reinterpret_cast<bf16x8*>(dst + 16) = dec_fp8(w[2], w[3]);
+  } else {  // BF16 weights and E4M3 weights of the static path are stored as they are
+    *reinterpret_cast<u32x4*>(dst) = w;
+  }
+}
+
+// bytes of decoded operand written per 16-byte packed chunk
+template <int F>
+constexpr int decoded_bytes() {
+  return (F == KF_INT4 || F == KF_NVFP4 || F == KF_MXFP4) ? 64 : ((F == KF_FP8) ? 32 : 16);
+}
+
+template <int F, int BM, int BN>
+__global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
+  using TF = TileFmt<F>;
+  constexpr int TM = BM / 32, TN = BN / 32;  // 16x16 tiles per wave (waves 2 x 2)
+  constexpr int LA = kBK * TF::XB / 16;       // 16-byte chunks per activation row per step
+  constexpr int NA = BM * LA / 256;           // activation loads per thread per step
+  constexpr int LB = TF::WSTEP / 16;          // 16-byte chunks per weight column per step
+  constexpr int CB = BN * LB;                 // weight chunks per step
+  constexpr int NB = (CB + 255) / 256;        // weight loads per thread per step
+  constexpr int DB = decoded_bytes<F>();
+  static_assert(NA * 256 == BM * LA, "activation tile must split evenly over 256 threads");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* As = smem;                         // [2][BM][ARS]
+  unsigned char* Bs = smem + 2 * BM * TF::ARS;      // [2][BN][BRS]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int M = a.M, N = a.N, K = a.K;
+
+  // XCD-aware tile order: consecutive workgroups go round-robin to the 8 XCDs;
+  // give each XCD a contiguous band of tiles (N fastest) so its resident
+  // tiles share activation rows.
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int G = gx * gy;
+  int b = blockIdx.y * gx + blockIdx.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int n0 = (b % gx) * BN, m0 = (b / gx) * BM;
+
+  const uint32_t wrow = (F == KF_BF16) ? 2u * (uint32_t)K : ((F == KF_FP8 || F == KF_FP8S) ? (uint32_t)K : (uint32_t)K / 2u);
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * wrow);
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * (uint32_t)K * (uint32_t)TF::XB);
+  uint32_t sbytes = 0;
+  if constexpr (F == KF_INT4) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 2u;
+  else if constexpr (F == KF_NVFP4) sbytes = (uint32_t)N * (uint32_t)(K / 16);
+  else if constexpr (F == KF_MXFP4) sbytes = (uint32_t)N * (uint32_t)(K / 32);
+  else if constexpr (F == KF_FP8 || F == KF_FP8S) sbytes = (uint32_t)N * 4u;
+  const __amdgpu_buffer_rsrc_t Sr = make_rsrc(a.scales ? a.scales : a.W, a.scales ? sbytes : 0u);
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+
+  const int KT = (K + kBK - 1) / kBK;
+
+  u32x4 xa[NA];
+  u32x4 wb[NB];
+  uint32_t sb[NB];
+
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      const int row = q * (256 / LA) + tid / LA;
+      const int kx = kt * kBK + (tid % LA) * (16 / TF::XB);
+      xa[q] = bload128(Xr, kx < K ? ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)kx) * (uint32_t)TF::XB : kOOB);
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int id = q * 256 + tid;
+      const int col = id / LB, part = id % LB;
+      const uint32_t n = (uint32_t)(n0 + col);
+      // K elements per 16-byte chunk: 4-bit 32, FP8 16, BF16 8; k0 is the chunk's first K
+      const int kpc = (F == KF_BF16) ? 8 : ((F == KF_FP8 || F == KF_FP8S) ? 16 : 32);
+      const int k0 = kt * kBK + part * kpc;
+      const bool ok = id < CB && k0 < K;
+      const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : ((F == KF_FP8 || F == KF_FP8S) ? (uint32_t)k0 : (uint32_t)k0 / 2u);
+      wb[q] = bload128(Wr, ok ? n * wrow + byte0 : kOOB);
+      if constexpr (F == KF_INT4) sb[q] = bload16(Sr, ok ? (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u : kOOB);
+      else if constexpr (F == KF_NVFP4) sb[q] = bload16(Sr, ok ? n * (uint32_t)(K / 16) + (uint32_t)(k0 / 16) : kOOB);
+      else if constexpr (F == KF_MXFP4) sb[q] = bload8(Sr, ok ? n * (uint32_t)(K / 32) + (uint32_t)(k0 / 32) : kOOB);
+      else sb[q] = 0u;
+    }
+  };
+  auto lstore = [&](int buf) {
+    unsigned char* A = As + buf * BM * TF::ARS;
+    unsigned char* B = Bs + buf * BN * TF::BRS;
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      const int row = q * (256 / LA) + tid / LA;
+      *reinterpret_cast<u32x4*>(A + row * TF::ARS + (tid % LA) * 16) = xa[q];
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int id = q * 256 + tid;
+      if (id < CB) {
+        const int col = id / LB, part = id % LB;
+        decode_store<F>(B + col * TF::BRS + part * DB, wb[q], sb[q]);
+      }
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    const unsigned char* A = As + buf * BM * TF::ARS;
+    const unsigned char* B = Bs + buf * BN * TF::BRS;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 32; ++kk) {
+      if constexpr (TF::ACT8) {
+        u32x2 af[TM], bf[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          af[i] = *reinterpret_cast<const u32x2*>(A + (wm * (BM / 2) + 16 * i + c) * TF::ARS + (kk * 32 + 8 * g));
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          bf[t] = *reinterpret_cast<const u32x2*>(B + (wn * (BN / 2) + 16 * t + c) * TF::BRS + (kk * 32 + 8 * g));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int t = 0; t < TN; ++t) acc[i][t] = mfma_fp8(af[i].x, af[i].y, bf[t].x, bf[t].y, acc[i][t]);
+      } else {
+        bf16x8 af[TM], bf[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(A + (wm * (BM / 2) + 16 * i + c) * TF::ARS + (kk * 32 + 8 * g) * 2);
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          bf[t] = *reinterpret_cast<const bf16x8*>(B + (wn * (BN / 2) + 16 * t + c) * TF::BRS + (kk * 32 + 8 * g) * 2);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int t = 0; t < TN; ++t) acc[i][t] = mfma_bf16(af[i], bf[t], acc[i][t]);
+      }
+    }
+    if (kt + 1 < KT) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds D[4g + r][c] of every 16x16 tile
+  float s1 = 1.0f;
+  if constexpr (F == KF_NVFP4) s1 = a.gscale[0];
+  if constexpr (F == KF_FP8S) s1 = a.act_scale[0];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int n = n0 + wn * (BN / 2) + 16 * t + c;
+    const float bias = bitsf(bload16(Br, (uint32_t)n * 2u) << 16);
+    float cs = 1.0f;
+    if constexpr (F == KF_FP8 || F == KF_FP8S) cs = bitsf(bload32(Sr, (uint32_t)n * 4u));
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
+        if (m < M && n < N) {
+          float y;
+          if constexpr (F == KF_FP8S) y = (acc[i][t][r] * s1) * cs;
+          else if constexpr (F == KF_FP8) y = acc[i][t][r] * cs;
+          else y = acc[i][t][r] * s1;
+          a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
+        }
+      }
+  }
+}
+
+template <int F, int BM, int BN>
+hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
+  constexpr int sm = tile_smem<F, BM, BN>();
+  static std::atomic<int> done{0};
+  auto k = k_gemm_tiled<F, BM, BN>;
+  hipError_t e = allow_smem(k, sm, done);
+  if (e != hipSuccess) return e;
+  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+  k<<<grid, 256, sm, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int F>
+hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (p.bm == 128 && p.bn == 128) return launch_tile<F, 128, 128>(a, s);
+  if (p.bm == 128) return launch_tile<F, 128, 64>(a, s);
+  if (p.bn == 128) return launch_tile<F, 64, 128>(a, s);
+  return launch_tile<F, 64, 64>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tiled(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  switch (kfmt) {
+    case KF_BF16: return launch_tiled_f<KF_BF16>(a, p, s);
+    case KF_INT4: return launch_tiled_f<KF_INT4>(a, p, s);
+    case KF_FP8: return launch_tiled_f<KF_FP8>(a, p, s);
+    case KF_NVFP4: return launch_tiled_f<KF_NVFP4>(a, p, s);
+    case KF_MXFP4: return launch_tiled_f<KF_MXFP4>(a, p, s);
+    case KF_FP8S: return launch_tiled_f<KF_FP8S>(a, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace wq

@@ -21,8 +21,11 @@ constexpr int kMaxSplit = 8;  // K splits across workgroups of one column tile
 // Tile configurations of the small-M kernel:
 //  kCfgSplit   : 64 columns x 4 waves per workgroup, K split across workgroups
 //  kCfgNoSplit : 16 columns x 12 waves per workgroup covering all of K
+//  kCfgTiled   : LDS-tiled GEMM for larger M (BM x BN tiles, weights decoded
+//                once per tile)
 constexpr int kCfgSplit = 0;
 constexpr int kCfgNoSplit = 1;
+constexpr int kCfgTiled = 2;
 
 struct LinearPlan {
   int cfg;        // kCfgSplit or kCfgNoSplit
@@ -32,6 +35,7 @@ struct LinearPlan {
   int spw;        // K macro-steps per wave whose loads are issued together
   int gx, gz;     // workgroups along N and along M
   int S;          // K splits across workgroups
+  int bm, bn;     // output tile of the tiled configuration
   size_t part_bytes, ws_bytes;  // split-K partials (0 without a split)
 };
 
@@ -50,6 +54,7 @@ struct LinearArgs {
 };
 
 hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
+hipError_t launch_gemm_tiled(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
 
 hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t N, int64_t K, void* codes, void* scales,
                            float* gscale, hipStream_t s);

@@ -38,165 +38,12 @@
 //  BF16  : the dense weight (the unquantized Linear), no decode.
 #include <atomic>
 
-#include "wq_device.hpp"
-#include "wq_internal.hpp"
+#include "wq_kernel_common.hpp"
 
 namespace wq {
 
 namespace {
 
-template <int F>
-struct FmtT;
-template <>
-struct FmtT<KF_BF16> {
-  static constexpr int KPL = 8;  // K elements per 16-byte weight chunk
-};
-template <>
-struct FmtT<KF_INT4> {
-  static constexpr int KPL = 32;
-};
-template <>
-struct FmtT<KF_FP8> {
-  static constexpr int KPL = 16;
-};
-template <>
-struct FmtT<KF_NVFP4> {
-  static constexpr int KPL = 32;
-};
-template <>
-struct FmtT<KF_MXFP4> {
-  static constexpr int KPL = 32;
-};
-template <>
-struct FmtT<KF_FP8S> {
-  static constexpr int KPL = 16;
-};
-
-template <int F>
-__device__ __forceinline__ int64_t kbyte(int64_t k) {
-  if constexpr (F == KF_BF16) return 2 * k;
-  else if constexpr (F == KF_FP8 || F == KF_FP8S) return k;
-  else return k / 2;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// INT4: 8 nibbles (K order 0..7) -> bf16 values 136 + code, K order kept.
-__device__ __forceinline__ bf16x8 dec_int4_biased(uint32_t w) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t v = u >> 4;
-  u32x4 p;
-  p.x = (__builtin_amdgcn_perm(v, u, 0x0C040C00u) & 0x000F000Fu) | 0x43004300u;
-  p.y = (__builtin_amdgcn_perm(v, u, 0x0C050C01u) & 0x000F000Fu) | 0x43004300u;
-  p.z = (__builtin_amdgcn_perm(v, u, 0x0C060C02u) & 0x000F000Fu) | 0x43004300u;
-  p.w = (__builtin_amdgcn_perm(v, u, 0x0C070C03u) & 0x000F000Fu) | 0x43004300u;
-  return as_bf16x8(p);
-}
-
-// E2M1 x 8 times an arbitrary fp32 scale d (the product is exact in bf16).
-__device__ __forceinline__ bf16x8 dec_fp4_mul(uint32_t w, float d) {
-  bf16x8 r;
-  f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  r[0] = (__bf16)(f0.x * d);
-  r[1] = (__bf16)(f0.y * d);
-  r[2] = (__bf16)(f1.x * d);
-  r[3] = (__bf16)(f1.y * d);
-  r[4] = (__bf16)(f2.x * d);
-  r[5] = (__bf16)(f2.y * d);
-  r[6] = (__bf16)(f3.x * d);
-  r[7] = (__bf16)(f3.y * d);
-  return r;
-}
-
-// E2M1 x 8 times a power-of-two scale p.
-__device__ __forceinline__ bf16x8 dec_fp4_pow2(uint32_t w, float p) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, p, 0);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, p, 1);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, p, 2);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, p, 3);
-  bf16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
-// E4M3 x 8 (two words) -> bf16, exact.
-__device__ __forceinline__ bf16x8 dec_fp8(uint32_t w0, uint32_t w1) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-  bf16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_fp8(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
-  const long a = (long)(((uint64_t)a1 << 32) | a0);
-  const long b = (long)(((uint64_t)b1 << 32) | b0);
-  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
-}
-
-// Buffer loads: an offset at or beyond the resource size reads as zero, which
-// masks the M, N and K tails without branches (a branch per masked load makes
-// the compiler wait for every outstanding load at each join).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
-
-constexpr uint32_t kOOB = 0x80000000u;  // beyond every resource (sizes are < 2^31)
-
-// Output epilogue: y = acc * column scale (+ bias) -> bf16 (nearest even).
-// Column scale: FP8 row scale, NVFP4 global scale, static FP8
-// act_scale * w_scale[n]; 1 otherwise.
-template <int F>
-struct Epilogue {
-  float scale1, scale2, bias;
-  __device__ __forceinline__ Epilogue(const LinearArgs& a, int en, uint32_t bias_bits, uint32_t cs_bits) {
-    bias = bitsf(bias_bits << 16);
-    scale2 = 1.0f;
-    if constexpr (F == KF_FP8) scale1 = bitsf(cs_bits);
-    else if constexpr (F == KF_NVFP4) scale1 = a.gscale[0];
-    else if constexpr (F == KF_FP8S) {
-      scale1 = a.act_scale[0];
-      scale2 = bitsf(cs_bits);
-    } else scale1 = 1.0f;
-  }
-  __device__ __forceinline__ void store(const LinearArgs& a, int m0, int en, int e, int E, int NT, float v) const {
-    const int m = m0 + e / NT;
-    if (e < E && m < a.M && en < a.N) {
-      float y = v * scale1;
-      if constexpr (F == KF_FP8S) y = y * scale2;
-      a.Y[(int64_t)m * a.N + en] = f32_to_bf16(y + bias);
-    }
-  }
-};
-
-// K-split plan of one workgroup: NW waves x SPW macro-steps each per block;
-// the S workgroups of a column tile interleave their blocks.
-//
-// Template parameters: F format, MT 16-row tiles, NTW 16-column tiles per wave,
-// NW waves per workgroup, SPW macro-steps whose loads are issued together.
 // Activation staging through LDS (XLDS): the MFMA operand layout wants lane
 // (g, c) to hold row c, K-chunk g, so loading it straight from a row-major X
 // touches 16 rows per load instruction.  With XLDS each wave instead loads
@@ -222,6 +69,11 @@ constexpr int smem_bytes(bool xlds) {
   return (red > xs ? red : xs) > 16 ? (red > xs ? red : xs) : 16;
 }
 
+// K-split plan of one workgroup: NW waves x SPW macro-steps each per block;
+// the S workgroups of a column tile interleave their blocks.
+//
+// Template parameters: F format, MT 16-row tiles, NTW 16-column tiles per wave,
+// NW waves per workgroup, SPW macro-steps whose loads are issued together.
 template <int F, int MT, int NTW, int NW, int SPW, bool XLDS>
 __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   constexpr int KPL = FmtT<F>::KPL;
@@ -523,15 +375,6 @@ constexpr int spw_split() {
   return (F == KF_BF16) ? 4 : ((F == KF_FP8 || F == KF_FP8S) ? 2 : 1);
 }
 
-// Dynamic LDS above 64 KiB must be allowed per kernel once per process.
-template <typename Kern>
-hipError_t allow_smem(Kern k, int bytes, std::atomic<int>& done) {
-  if (bytes <= 65536 || done.load(std::memory_order_acquire)) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) done.store(1, std::memory_order_release);
-  return e;
-}
-
 template <int F, int MT>
 hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   dim3 grid(p.gx, p.S, p.gz);
@@ -582,6 +425,26 @@ int spw_of(int kfmt, int cfg) {
 
 LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
   LinearPlan p{};
+  if (M > 64) {
+    // MFMA-bound: LDS-tiled GEMM; the largest tile that still gives about
+    // 192 workgroups
+    p.cfg = kCfgTiled;
+    p.S = 1;
+    p.bm = 64;
+    p.bn = 64;
+    const int cand[3][2] = {{128, 128}, {128, 64}, {64, 128}};
+    for (const auto& cb : cand) {
+      const int64_t tiles = ((M + cb[0] - 1) / cb[0]) * ((N + cb[1] - 1) / cb[1]);
+      if (tiles >= 192) {
+        p.bm = cb[0];
+        p.bn = cb[1];
+        break;
+      }
+    }
+    p.part_bytes = 0;
+    p.ws_bytes = 0;
+    return p;
+  }
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.gz = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
   // No-split (16 columns x all of K per workgroup) whenever it yields enough
@@ -615,6 +478,7 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (p.cfg == kCfgTiled) return launch_gemm_tiled(kfmt, a, p, s);
   switch (kfmt) {
     case KF_BF16: return launch_f<KF_BF16>(a, p, s);
     case KF_INT4: return launch_f<KF_INT4>(a, p, s);
