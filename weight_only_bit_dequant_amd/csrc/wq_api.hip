@@ -185,6 +185,8 @@ static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int6
     const int64_t xbytes = kfmt == wq::KF_FP8S ? M * K : 2 * M * K;
     if (wbytes >= kMaxBufferBytes || xbytes >= kMaxBufferBytes)
       return fail(WQ_EUNSUPPORTED, "weight or activation buffer of 2^31 bytes or more");
+    // tile overhang past the last row/column must not wrap a 32-bit offset
+    if (K >= ((int64_t)1 << 22)) return fail(WQ_EUNSUPPORTED, "K of 2^22 or more");
   }
   if (!X || !W || !Y) return fail(WQ_EINVAL, "null X, weight or Y");
   if (fmt != WQ_BF16 && !scales) return fail(WQ_EINVAL, "null scales");

@@ -76,13 +76,15 @@ __device__ __forceinline__ uint32_t e2m1_encode(float x) {
   return sign | code;
 }
 
-// Decoders (exact).
+// Decoders (exact).  Written with selects only: a data-dependent branch in a
+// kernel's main loop makes the compiler drain every memory load in flight.
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float mag = (e == 0u) ? (float)m * 0.001953125f  // m * 2^-9
-                        : bitsf(((e + 120u) << 23) | (m << 20));
-  if ((c & 0x7Fu) == 0x7Fu) mag = __builtin_nanf("");
-  return (c & 0x80u) ? -mag : mag;
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float sub = (float)m * 0.001953125f;  // m * 2^-9
+  const float nrm = bitsf(((e + 120u) << 23) | (m << 20));
+  float mag = (e == 0u) ? sub : nrm;
+  mag = ((c & 0x7Fu) == 0x7Fu) ? __builtin_nanf("") : mag;
+  return bitsf(fbits(mag) | ((c & 0x80u) << 24));
 }
 
 __device__ __forceinline__ float e2m1_decode(uint32_t c) {
@@ -91,11 +93,10 @@ __device__ __forceinline__ float e2m1_decode(uint32_t c) {
   return (c & 8u) ? -v : v;
 }
 
-// 2^(c - 127) for an E8M0 code (0xFF -> NaN).
+// 2^(c - 127) for an E8M0 code (0xFF -> NaN; 0 -> 2^-127, an fp32 subnormal).
 __device__ __forceinline__ float e8m0_decode(uint32_t c) {
-  if (c == 0xFFu) return __builtin_nanf("");
-  if (c == 0u) return bitsf(0x00400000u);  // 2^-127 (fp32 subnormal)
-  return bitsf(c << 23);
+  const uint32_t bits = (c == 0u) ? 0x00400000u : ((c == 0xFFu) ? 0x7FC00000u : (c << 23));
+  return bitsf(bits);
 }
 
 __device__ __forceinline__ float clampf(float x, float lo, float hi) { return fminf(fmaxf(x, lo), hi); }

@@ -24,7 +24,11 @@ namespace wq {
 
 namespace {
 
-constexpr int kBK = 64;  // K elements per step
+constexpr int kBK = 64;    // K elements per step
+#ifndef WQ_TILE_STAGES
+#define WQ_TILE_STAGES 4
+#endif
+constexpr int kStages = WQ_TILE_STAGES;  // global-load steps in flight
 
 template <int F>
 struct TileFmt {
@@ -84,7 +88,7 @@ constexpr int decoded_bytes() {
   return (F == KF_INT4 || F == KF_NVFP4 || F == KF_MXFP4) ? 64 : ((F == KF_FP8) ? 32 : 16);
 }
 
-template <int F, int BM, int BN>
+template <int F, int BM, int BN, int STG>
 __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
   using TF = TileFmt<F>;
   constexpr int TM = BM / 32, TN = BN / 32;  // 16x16 tiles per wave (waves 2 x 2)
@@ -126,35 +130,40 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
 
   const int KT = (K + kBK - 1) / kBK;
 
-  u32x4 xa[NA];
-  u32x4 wb[NB];
-  uint32_t sb[NB];
+  // STG register stages of global loads are in flight: the loads of step k
+  // live in stage k % STG from the moment they are issued (STG steps ahead)
+  // until their decode into LDS.
+  u32x4 xa[STG][NA];
+  u32x4 wb[STG][NB];
+  uint32_t sb[STG][NB];
 
-  auto gload = [&](int kt) {
+  auto gload = [&](int kt, u32x4 (&xa)[NA], u32x4 (&wb)[NB], uint32_t (&sb)[NB]) {
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
       const int row = q * (256 / LA) + tid / LA;
       const int kx = kt * kBK + (tid % LA) * (16 / TF::XB);
-      xa[q] = bload128(Xr, kx < K ? ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)kx) * (uint32_t)TF::XB : kOOB);
+      xa[q] = bload128(Xr, off_if(kx < K, ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)kx) * (uint32_t)TF::XB));
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      const int id = q * 256 + tid;
+      // threads beyond the chunk count repeat a chunk (identical bytes): no
+      // divergent branch, which would make the compiler drain every load
+      const int id = (q * 256 + tid) % CB;
       const int col = id / LB, part = id % LB;
       const uint32_t n = (uint32_t)(n0 + col);
       // K elements per 16-byte chunk: 4-bit 32, FP8 16, BF16 8; k0 is the chunk's first K
       const int kpc = (F == KF_BF16) ? 8 : ((F == KF_FP8 || F == KF_FP8S) ? 16 : 32);
       const int k0 = kt * kBK + part * kpc;
-      const bool ok = id < CB && k0 < K;
+      const bool ok = k0 < K;
       const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : ((F == KF_FP8 || F == KF_FP8S) ? (uint32_t)k0 : (uint32_t)k0 / 2u);
-      wb[q] = bload128(Wr, ok ? n * wrow + byte0 : kOOB);
-      if constexpr (F == KF_INT4) sb[q] = bload16(Sr, ok ? (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u : kOOB);
-      else if constexpr (F == KF_NVFP4) sb[q] = bload16(Sr, ok ? n * (uint32_t)(K / 16) + (uint32_t)(k0 / 16) : kOOB);
-      else if constexpr (F == KF_MXFP4) sb[q] = bload8(Sr, ok ? n * (uint32_t)(K / 32) + (uint32_t)(k0 / 32) : kOOB);
+      wb[q] = bload128(Wr, off_if(ok, n * wrow + byte0));
+      if constexpr (F == KF_INT4) sb[q] = bload16(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u));
+      else if constexpr (F == KF_NVFP4) sb[q] = bload16(Sr, off_if(ok, n * (uint32_t)(K / 16) + (uint32_t)(k0 / 16)));
+      else if constexpr (F == KF_MXFP4) sb[q] = bload8(Sr, off_if(ok, n * (uint32_t)(K / 32) + (uint32_t)(k0 / 32)));
       else sb[q] = 0u;
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const u32x4 (&xa)[NA], const u32x4 (&wb)[NB], const uint32_t (&sb)[NB]) {
     unsigned char* A = As + buf * BM * TF::ARS;
     unsigned char* B = Bs + buf * BN * TF::BRS;
 #pragma unroll
@@ -164,13 +173,20 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      const int id = q * 256 + tid;
-      if (id < CB) {
-        const int col = id / LB, part = id % LB;
-        decode_store<F>(B + col * TF::BRS + part * DB, wb[q], sb[q]);
-      }
+      const int id = (q * 256 + tid) % CB;
+      const int col = id / LB, part = id % LB;
+      decode_store<F>(B + col * TF::BRS + part * DB, wb[q], sb[q]);
     }
   };
+
+  // epilogue operands of this lane's columns, loaded up front
+  uint32_t bias_bits[TN], cs_bits[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const uint32_t n = (uint32_t)(n0 + wn * (BN / 2) + 16 * t + c);
+    bias_bits[t] = bload16(Br, n * 2u);
+    cs_bits[t] = (F == KF_FP8 || F == KF_FP8S) ? bload32(Sr, n * 4u) : 0x3F800000u;
+  }
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -178,13 +194,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+  auto compute = [&](int buf) {
     const unsigned char* A = As + buf * BM * TF::ARS;
     const unsigned char* B = Bs + buf * BN * TF::BRS;
 #pragma unroll
@@ -215,32 +225,59 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
           for (int t = 0; t < TN; ++t) acc[i][t] = mfma_bf16(af[i], bf[t], acc[i][t]);
       }
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // The step count is padded to a multiple of STG: steps past K read zeros
+  // (their loads fall outside the buffers) and add nothing, which keeps the
+  // loop body free of branches -- a branch makes the compiler drain all loads
+  // in flight.  STG is even, so the LDS buffer index kt % 2 = st % 2 is a
+  // compile-time constant.
+  static_assert(STG % 2 == 0, "even number of load stages");
+  const int KTP = (KT + STG - 1) / STG * STG;
+
+  // prologue: steps 0 .. STG-1 in flight, step 0 decoded into LDS buffer 0,
+  // then its register stage refilled with step STG
+#pragma unroll
+  for (int st = 0; st < STG; ++st) gload(st, xa[st], wb[st], sb[st]);
+  lstore(0, xa[0], wb[0], sb[0]);
+  gload(STG, xa[0], wb[0], sb[0]);
+  __syncthreads();
+
+  // step kt computes from LDS buffer kt % 2, decodes step kt + 1 (register
+  // stage (kt + 1) % STG) into the other buffer and refills that stage with
+  // step kt + 1 + STG
+  for (int kt0 = 0; kt0 < KTP; kt0 += STG) {
+#pragma unroll
+    for (int st = 0; st < STG; ++st) {
+      const int kt = kt0 + st;
+      const int nx = (st + 1) % STG;
+      compute(st & 1);
+      lstore((st + 1) & 1, xa[nx], wb[nx], sb[nx]);
+      gload(kt + 1 + STG, xa[nx], wb[nx], sb[nx]);
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue: lane holds D[4g + r][c] of every 16x16 tile
+  // ---- epilogue: lane holds D[4g + r][c] of every 16x16 tile; the column
+  // operands were fetched before the main loop
   float s1 = 1.0f;
   if constexpr (F == KF_NVFP4) s1 = a.gscale[0];
   if constexpr (F == KF_FP8S) s1 = a.act_scale[0];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int n = n0 + wn * (BN / 2) + 16 * t + c;
-    const float bias = bitsf(bload16(Br, (uint32_t)n * 2u) << 16);
-    float cs = 1.0f;
-    if constexpr (F == KF_FP8 || F == KF_FP8S) cs = bitsf(bload32(Sr, (uint32_t)n * 4u));
+    const float bias = bitsf(bias_bits[t] << 16);
+    const float cs = bitsf(cs_bits[t]);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
-        if (m < M && n < N) {
-          float y;
-          if constexpr (F == KF_FP8S) y = (acc[i][t][r] * s1) * cs;
-          else if constexpr (F == KF_FP8) y = acc[i][t][r] * cs;
-          else y = acc[i][t][r] * s1;
-          a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
-        }
+        float y;
+        if constexpr (F == KF_FP8S) y = (acc[i][t][r] * s1) * cs;
+        else if constexpr (F == KF_FP8) y = acc[i][t][r] * cs;
+        else y = acc[i][t][r] * s1;
+        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
       }
   }
 }
@@ -249,7 +286,7 @@ template <int F, int BM, int BN>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   constexpr int sm = tile_smem<F, BM, BN>();
   static std::atomic<int> done{0};
-  auto k = k_gemm_tiled<F, BM, BN>;
+  auto k = k_gemm_tiled<F, BM, BN, kStages>;
   hipError_t e = allow_smem(k, sm, done);
   if (e != hipSuccess) return e;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);

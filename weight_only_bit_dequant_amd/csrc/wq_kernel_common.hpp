@@ -130,6 +130,11 @@ __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 constexpr uint32_t kOOB = 0x80000000u;  // beyond every resource (sizes are < 2^31)
 
+// `off` when `ok`, else an offset past every resource -- computed with bit
+// operations so the compiler cannot split the load into guarded branches
+// (each branch join would drain the loads in flight).
+__device__ __forceinline__ uint32_t off_if(bool ok, uint32_t off) { return off | ((uint32_t)(!ok) << 31); }
+
 // Output epilogue: y = acc * column scale (+ bias) -> bf16 (nearest even).
 // Column scale: FP8 row scale, NVFP4 global scale, static FP8
 // act_scale * w_scale[n]; 1 otherwise.

@@ -134,10 +134,10 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
         const uint32_t n = (uint32_t)(n0 + 16 * t + c);
-        w[st][t] = bload128(Wr, kv ? n * wrow + (uint32_t)kbyte<F>(kl) : kOOB);
-        if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, kv ? (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u : kOOB);
-        else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, kv ? n * (uint32_t)(K / 16) + (uint32_t)(kl / 16) : kOOB);
-        else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, kv ? n * (uint32_t)(K / 32) + (uint32_t)(kl / 32) : kOOB);
+        w[st][t] = bload128(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
+        if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u));
+        else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, off_if(kv, n * (uint32_t)(K / 16) + (uint32_t)(kl / 16)));
+        else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, off_if(kv, n * (uint32_t)(K / 32) + (uint32_t)(kl / 32)));
         else sc[st][t] = 0u;
       }
 #pragma unroll
@@ -150,11 +150,11 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
             const int q = i * XL + j;
             const uint32_t row = (uint32_t)(m0 + q * XS::R + lane / XS::L);
             const int kx = (blk * SPW + st) * MACRO + (lane % XS::L) * (16 / XS::XB);
-            xv[st][i][j] = bload128(Xr, kx < K ? (row * (uint32_t)K + (uint32_t)kx) * (uint32_t)XS::XB : kOOB);
+            xv[st][i][j] = bload128(Xr, off_if(kx < K, (row * (uint32_t)K + (uint32_t)kx) * (uint32_t)XS::XB));
           } else if constexpr (ACT8) {
-            xv[st][i][j] = bload128(Xr, kv ? m * (uint32_t)K + (uint32_t)kl : kOOB);
+            xv[st][i][j] = bload128(Xr, off_if(kv, m * (uint32_t)K + (uint32_t)kl));
           } else {
-            xv[st][i][j] = bload128(Xr, kv ? (m * (uint32_t)K + (uint32_t)kl + 8u * j) * 2u : kOOB);
+            xv[st][i][j] = bload128(Xr, off_if(kv, (m * (uint32_t)K + (uint32_t)kl + 8u * j) * 2u));
           }
         }
       }
