@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--hot", action="store_true", help="one weight copy per format (cache-resident)")
     p.add_argument("--only", default=None, help="time only this format's kernel (profiling aid)")
+    p.add_argument("--no-sweep", action="store_true", help="skip the M sweep (MXFP4 M=1..4096, static FP8 M=4096)")
     return p.parse_args()
 
 
@@ -108,6 +109,59 @@ def cpu_baseline(seconds_budget=12.0):
         "seconds_per_format": {k: round(v, 4) for k, v in per.items()},
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def m_sweep(layers, dev, capture):
+    """The other workload points (reported beside the M=32 line): MXFP4 at
+    M in {1, 32, 256, 4096} and the static-FP8 layer at M=4096, each timed as a
+    graph of back-to-back launches over the same cold weight copies.  Large M
+    is bound by the matrix cores: FLOP/s against the dense bf16 (MXFP4) or
+    FP8 (static) peak."""
+    import torch
+
+    from weight_only_bit_dequant_amd import synth, wq
+
+    res = {}
+    peak = {"mxfp4": 2500.0, "static_fp8": 5000.0}  # dense TFLOP/s (bf16 / fp8)
+    for fmt, Ms in (("mxfp4", (1, 32, 256, 4096)), ("static_fp8", (32, 4096))):
+        lay = layers[fmt]
+        for Mv in Ms:
+            X = synth.as_torch_bf16(synth.activations(Mv, K, synth.SEED_X + synth.WORKLOADS[fmt]["cfg"]), dev)
+            Y = torch.empty((Mv, N), dtype=torch.bfloat16, device=dev)
+            if fmt == "static_fp8":
+                ws = torch.zeros(max(1, wq.wq_fp8_static_workspace(Mv, N, K)), dtype=torch.uint8, device=dev)
+            else:
+                ws = torch.zeros(max(1, wq.wq_linear_workspace("mxfp4", Mv, N, K)), dtype=torch.uint8, device=dev)
+
+            def run(first, count, lay=lay, X=X, Y=Y, ws=ws, fmt=fmt):
+                for i in range(first, first + count):
+                    r = lay["reps"][i % len(lay["reps"])]
+                    if fmt == "static_fp8":
+                        wq.wq_fp8_static_linear(X, lay["act_scale"], r["packed"], r["scales"], None, Y, ws)
+                    else:
+                        wq.wq_linear("mxfp4", X, r["packed"], r["scales"], None, lay["bias"], N, Y, ws)
+
+            reps = 200 if Mv <= 256 else 30
+            g = capture(run, reps)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            flop = 2.0 * Mv * N * K
+            eff = effective_bytes(fmt)
+            res[f"{fmt}_M{Mv}"] = {
+                "us_per_launch": round(us, 3),
+                "TFLOPs": round(flop / (us * 1e-6) / 1e12, 2),
+                "pct_mfma_peak": round(100.0 * flop / (us * 1e-6) / 1e12 / peak[fmt], 2),
+                "effective_TBps": round(eff / (us * 1e-6) / 1e12, 4),
+                "launches": 2 if fmt == "static_fp8" else 1,
+            }
+            del g
+    return res
 
 
 def main():
@@ -216,6 +270,8 @@ def main():
         }
         del g
 
+    sweep = None if (args.no_sweep or args.only) else m_sweep(layers, dev, capture)
+
     dominant = max(per_format, key=lambda f: per_format[f]["us_per_launch"])
     d = per_format[dominant]
     achieved = d["algorithmic_bytes"] / (d["us_per_launch"] * 1e-6) / 1e9
@@ -243,6 +299,8 @@ def main():
         "per_format": per_format,
         "wall_s_timed": round(t_wall, 4),
     }
+    if sweep is not None:
+        out["m_sweep"] = sweep
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

@@ -24,11 +24,15 @@ namespace wq {
 
 namespace {
 
-constexpr int kBK = 64;    // K elements per step
-#ifndef WQ_TILE_STAGES
-#define WQ_TILE_STAGES 4
-#endif
-constexpr int kStages = WQ_TILE_STAGES;  // global-load steps in flight
+constexpr int kBK = 64;  // K elements per step
+
+// Global-load steps in flight per tile shape (measured on MI355X): the large
+// 128 x 128 tile keeps two stages so two workgroups fit per CU (registers);
+// smaller tiles, used when there are few tiles, keep four.
+template <int BM, int BN>
+constexpr int tile_stages() {
+  return (BM == 128 && BN == 128) ? 2 : 4;
+}
 
 template <int F>
 struct TileFmt {
@@ -286,7 +290,7 @@ template <int F, int BM, int BN>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   constexpr int sm = tile_smem<F, BM, BN>();
   static std::atomic<int> done{0};
-  auto k = k_gemm_tiled<F, BM, BN, kStages>;
+  auto k = k_gemm_tiled<F, BM, BN, tile_stages<BM, BN>()>;
   hipError_t e = allow_smem(k, sm, done);
   if (e != hipSuccess) return e;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
