@@ -29,7 +29,7 @@ constexpr int kCfgTiled = 2;
 
 struct LinearPlan {
   int cfg;        // kCfgSplit or kCfgNoSplit
-  int mt;         // 16-row MFMA tiles per workgroup (1, 2 or 4)
+  int mt;         // 16-row MFMA tiles per workgroup (1 or 2)
   int ntw;        // 16-column tiles per wave (= per workgroup)
   int nwaves;     // waves per workgroup
   int spw;        // K macro-steps per wave whose loads are issued together

@@ -137,17 +137,25 @@ __device__ __forceinline__ uint32_t off_if(bool ok, uint32_t off) { return off |
 
 // Output epilogue: y = acc * column scale (+ bias) -> bf16 (nearest even).
 // Column scale: FP8 row scale, NVFP4 global scale, static FP8
-// act_scale * w_scale[n]; 1 otherwise.
+// act_scale * w_scale[n]; 1 otherwise.  The tensor-wide factor (NVFP4 global,
+// static act_scale) is read by uniform_scale() at kernel start so that its
+// load travels with the main loads instead of after the reduction.
 template <int F>
 struct Epilogue {
   float scale1, scale2, bias;
-  __device__ __forceinline__ Epilogue(const LinearArgs& a, int en, uint32_t bias_bits, uint32_t cs_bits) {
+  __device__ __forceinline__ static float uniform_scale(const LinearArgs& a) {
+    if constexpr (F == KF_NVFP4) return a.gscale[0];
+    else if constexpr (F == KF_FP8S) return a.act_scale[0];
+    else return 1.0f;
+  }
+  __device__ __forceinline__ Epilogue(int en, uint32_t bias_bits, uint32_t cs_bits, float uscale) {
+    (void)en;
     bias = bitsf(bias_bits << 16);
     scale2 = 1.0f;
     if constexpr (F == KF_FP8) scale1 = bitsf(cs_bits);
-    else if constexpr (F == KF_NVFP4) scale1 = a.gscale[0];
+    else if constexpr (F == KF_NVFP4) scale1 = uscale;
     else if constexpr (F == KF_FP8S) {
-      scale1 = a.act_scale[0];
+      scale1 = uscale;
       scale2 = bitsf(cs_bits);
     } else scale1 = 1.0f;
   }
@@ -160,7 +168,6 @@ struct Epilogue {
     }
   }
 };
-
 
 // Dynamic LDS above 64 KiB must be allowed per kernel once per process.
 template <typename Kern>

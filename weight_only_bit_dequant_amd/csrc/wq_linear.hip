@@ -1,25 +1,29 @@
-// Dequant-GEMM for small and moderate M: Y = X . deq(W)^T (+ b).
+// Dequant-GEMM for small M (M <= 64): Y = X . deq(W)^T (+ b).
 //
 // Every weight-only page's intro describes the engine it wants: the weight stays
 // packed in device memory and a dequantization prologue feeds a high-precision
 // GEMM while activations stay bf16 (NVFP4 adds a two-level block x global
 // scale).  The static-FP8 page's intro runs the GEMM itself in FP8.  Here:
 //
-//  * one workgroup = 4 waves = 64 output columns x a contiguous K range;
-//    each wave owns a quarter of that K range (split-K inside the workgroup);
-//  * per K macro-step each lane issues one 16-byte load per 16-column tile of
-//    packed weight and 16-byte loads of its activation rows straight into
-//    registers (no LDS staging at small M: every activation element is used
-//    by exactly the 64 columns of this workgroup);
+//  * no-split tiles (wide layers): one workgroup = 12 waves = 16 output
+//    columns x all of K; each wave owns a contiguous K range (split-K inside
+//    the workgroup).  Split tiles (narrow layers): 4 waves = 64 columns x a K
+//    range, with the K ranges of one column tile spread over S workgroups;
+//  * each wave issues every load of its K range (packed weight, block scales,
+//    activations, bias, column scale) before the first wait, as buffer loads
+//    whose out-of-range offsets read zero (no branches around loads);
+//  * activations (M <= 32 rows per workgroup) are loaded with contiguous
+//    16-byte loads into a private LDS slot per wave and read back in the
+//    MFMA operand layout;
 //  * codes are decoded in registers and fed to v_mfma_f32_16x16x32_bf16
 //    (v_mfma_f32_16x16x32_fp8_fp8 for the static path) with fp32
 //    accumulation.  Lane (g, c) with g = lane/16, c = lane%16 supplies
 //    8 consecutive K of its own 16-byte chunk to each MFMA, so the K order
 //    inside an MFMA is a permutation shared by both operands;
-//  * wave partials are reduced through LDS; with S > 1 K-splits the
-//    workgroups of one column tile write fp32 partials to the workspace and
-//    the last one to arrive (device-scope counter) sums them in a fixed
-//    order, applies the epilogue and resets the counter;
+//  * every wave writes its partial tile to LDS; after one barrier each thread
+//    sums the wave partials of its output in a fixed order.  With S > 1 the
+//    workgroup partials go to the workspace and k_splitk_reduce, launched
+//    next on the same stream, sums them;
 //  * epilogue: x row/global scale, + bias, one nearest-even rounding to bf16.
 //
 // Decode per format (all exact in bf16):
@@ -61,12 +65,14 @@ struct XStage {
   static constexpr int R = 64 / L;                    // rows per load instruction
 };
 
+// LDS: [activation slots of the NW waves (XLDS)][NW wave partials, fp32]
+template <int F, int MT, int NTW, int NW>
+constexpr int xslots_bytes(bool xlds) {
+  return xlds ? NW * XStage<F, MT>::SLOT : 0;
+}
 template <int F, int MT, int NTW, int NW>
 constexpr int smem_bytes(bool xlds) {
-  const int E = MT * 16 * 16 * NTW;
-  const int red = (NW - 1) * E * 4;
-  const int xs = xlds ? NW * XStage<F, MT>::SLOT : 0;
-  return (red > xs ? red : xs) > 16 ? (red > xs ? red : xs) : 16;
+  return xslots_bytes<F, MT, NTW, NW>(xlds) + NW * (MT * 16 * 16 * NTW) * 4;
 }
 
 // K-split plan of one workgroup: NW waves x SPW macro-steps each per block;
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   using XS = XStage<F, MT>;
   static_assert(!XLDS || XS::R * MT * XL == 16 * MT, "XLDS: load instructions must cover the slice rows");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* red = reinterpret_cast<float*>(smem);
+  float* red = reinterpret_cast<float*>(smem + xslots_bytes<F, MT, NTW, NW>(XLDS));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -114,6 +120,7 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   const uint32_t bias_bits = bload16(Br, (uint32_t)en * 2u);
   uint32_t cs_bits = 0x3F800000u;  // 1.0f
   if constexpr (F == KF_FP8 || F == KF_FP8S) cs_bits = bload32(Sr, (uint32_t)en * 4u);
+  const float uscale = Epilogue<F>::uniform_scale(a);
 
   f32x4 acc[MT][NTW];
 #pragma unroll
@@ -261,46 +268,33 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     }
   }
 
-  // ---- reduce the wave partials: waves 1.. through LDS into wave 0, which
-  // leaves the workgroup total in the first LDS slice
-  if constexpr (XLDS) __syncthreads();  // the activation slots are reused
-  if (wave > 0) {
-    float* dst = red + (wave - 1) * E;
+  // ---- reduce the wave partials: every wave stores its tile (one 16-byte
+  // vector per lane and MFMA tile), then thread tid sums the NW partials of
+  // the outputs e = tid + q * NTHR (row-major in the workgroup tile, column
+  // n0 + tid % NT) in wave order.
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int t = 0; t < NTW; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * NT + 16 * t + c] = acc[i][t][r];
-  }
+    for (int t = 0; t < NTW; ++t)
+      *reinterpret_cast<f32x4*>(red + ((wave * MT * NTW + i * NTW + t) * 64 + lane) * 4) = acc[i][t];
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int t = 0; t < NTW; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = (16 * i + 4 * g + r) * NT + 16 * t + c;
-          float v = acc[i][t][r];
-#pragma unroll
-          for (int w2 = 0; w2 < NW - 1; ++w2) v += red[w2 * E + e];
-          red[e] = v;
-        }
-  }
-  __syncthreads();
-
-  // ---- epilogue: column scale, bias, one rounding to bf16.  Thread tid owns
-  // the outputs e = tid + q * NTHR (q < EPT), all in column n0 + tid % NT.
   constexpr int EPT = (E + NTHR - 1) / NTHR;
   float v[EPT];
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
     const int e = tid + q * NTHR;
-    v[q] = (e < E) ? red[e] : 0.f;
+    const int row = e / NT, col = e % NT;
+    // lane (g, c) of MFMA tile (i, t) holds rows 16i + 4g + r, column 16t + c
+    const int idx = (((row >> 4) * NTW + (col >> 4)) * 64 + 16 * ((row >> 2) & 3) + (col & 15)) * 4 + (row & 3);
+    float sum = 0.f;
+    if (e < E) {
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) sum += red[w2 * E + idx];
+    }
+    v[q] = sum;
   }
   if (S == 1) {
-    const Epilogue<F> ep(a, en, bias_bits, cs_bits);
+    const Epilogue<F> ep(en, bias_bits, cs_bits, uscale);
 #pragma unroll
     for (int q = 0; q < EPT; ++q) ep.store(a, m0, en, tid + q * NTHR, E, NT, v[q]);
     return;
@@ -358,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void k_splitk_reduce(LinearArgs a, int S) 
   for (int s2 = 0; s2 < kMaxSplit; ++s2)
 #pragma unroll
     for (int q = 0; q < EPT; ++q) v[q] += bitsf(pv[s2][q / 4][q % 4]);
-  const Epilogue<F> ep(a, en, bias_bits, cs_bits);
+  const Epilogue<F> ep(en, bias_bits, cs_bits, Epilogue<F>::uniform_scale(a));
 #pragma unroll
   for (int q = 0; q < EPT; ++q) ep.store(a, m0, en, tid + q * NTHR, E, NT, v[q]);
 }
@@ -382,28 +376,22 @@ hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
     constexpr int sm = smem_bytes<F, MT, 4, 4>(false);
     k_linear<F, MT, 4, 4, spw_split<F>(), false><<<grid, 256, sm, s>>>(a, p.S);
     if (p.S > 1) k_splitk_reduce<F, MT, 4, 4><<<dim3(p.gx, 1, p.gz), 256, 0, s>>>(a, p.S);
-  } else if constexpr (MT <= 2) {
+  } else {
     // no-split tiles with activations staged through LDS
     constexpr int sm = smem_bytes<F, MT, 1, 12>(true);
+    static_assert(sm <= 160 * 1024, "no-split tile exceeds the LDS of a CU");
     static std::atomic<int> done{0};
     auto k = k_linear<F, MT, 1, 12, spw_nosplit<F>(), true>;
     hipError_t e = allow_smem(k, sm, done);
     if (e != hipSuccess) return e;
     k<<<grid, 768, sm, s>>>(a, p.S);
-  } else {
-    constexpr int sm = smem_bytes<F, MT, 1, 12>(false);
-    k_linear<F, MT, 1, 12, spw_nosplit<F>(), false><<<grid, 768, sm, s>>>(a, p.S);
   }
   return hipGetLastError();
 }
 
 template <int F>
 hipError_t launch_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  switch (p.mt) {
-    case 1: return launch_mt<F, 1>(a, p, s);
-    case 2: return launch_mt<F, 2>(a, p, s);
-    default: return launch_mt<F, 4>(a, p, s);
-  }
+  return p.mt == 1 ? launch_mt<F, 1>(a, p, s) : launch_mt<F, 2>(a, p, s);
 }
 
 int kpl_of(int kfmt) {
@@ -445,7 +433,11 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
     p.ws_bytes = 0;
     return p;
   }
-  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  // 16 or 32 rows per workgroup; 33..64 rows take two row blocks (grid z)
+  // that read the same packed columns.  Workgroup ids of one column tile
+  // differ by gx, so with gx a multiple of 8 both blocks run on the same XCD
+  // (workgroups are dealt to the 8 XCDs round robin) and share its L2 copy.
+  p.mt = M <= 16 ? 1 : 2;
   p.gz = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
   // No-split (16 columns x all of K per workgroup) whenever it yields enough
   // workgroups to cover the chip; otherwise 64-column tiles with K split
