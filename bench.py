@@ -4,21 +4,38 @@
 One step = one pass of the whole hot path over one batch X[32, 3072] (bf16):
 the four weight-only dequant-GEMMs (INT4 group-128, FP8 per-row, NVFP4, MXFP4;
 each y = x . deq(W)^T + b, bf16 out) and the static-FP8 Linear (activation Q to
-E4M3 + FP8 GEMM).  Weights stay packed in HBM; every launch reads a different
-copy of the packed weight + scales (copies per format total >= 512 MiB, twice
-the 256 MB Infinity Cache), so the weight stream is cold.  X and bias stay warm
-(they are the previous layer's output).  The timed steps run as one HIP graph
-replay between two synchronizations.
+E4M3, then the FP8 GEMM).  Weights stay packed in HBM; every launch reads a
+different copy of the packed weight + scales (copies per format total
+>= 512 MiB, twice the 256 MB Infinity Cache), so the weight stream is cold.  X
+and bias stay warm (they are the previous layer's output).
+
+Timed region (one pair of device synchronizations): the K-step graph, then,
+for each single kernel of the step, a graph of K back-to-back launches of it
+alone, then a graph of K launches of a plain read-only stream of each format's
+weight bytes over the same kind of cold rotation (the achievable ceiling), and
+each format's kernel on one hot copy.  HIP events on the replay stream
+separate the parts; a kernel's figure is its graph time / K.
 
 Metric: effective weight-stream bandwidth = (packed weight + scale bytes) /
-time.  `value` is the whole step's effective bytes / ms_per_step; per-format
-kernel figures come from HIP-event-timed graphs of back-to-back launches of that
-kernel alone (its average launch duration).
+time.  `value` is the step's effective bytes / ms_per_step.  `roofline` is for
+the slowest single kernel: algorithmic bytes (weights, scales, X, bias, Y) per
+launch / its average duration.  `traffic` comes from the committed
+FETCH_SIZE / WRITE_SIZE counter profile when the kernel sources still hash to
+the value recorded there, else null.
+
+Also: `python bench.py --trace-summary DIR --out FILE` and
+`python bench.py --counters-summary FETCH_DIR WRITE_DIR --out FILE` turn
+rocprofv3 output directories of this script into the text summaries kept
+under profiles/.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,7 +46,12 @@ METRIC = "effective weight-stream TB/s (+% HBM peak), 3072→4096 Linear, M=32, 
 HBM_PEAK_GBS = 8000.0
 M, N, K = 32, 4096, 3072
 FORMATS = ["int4", "fp8", "nvfp4", "mxfp4"]
+STEP = FORMATS + ["static_fp8"]                      # the step: static_fp8 = act Q + FP8 GEMM
+KERNELS = FORMATS + ["static_q", "static_gemm"]      # single kernels of the step
 COLD_BYTES = 512 << 20
+STREAM_POOL = 768 << 20
+CSRC = os.path.join(ROOT, "weight_only_bit_dequant_amd", "csrc")
+COUNTERS_PROFILE = os.path.join(ROOT, "profiles", "linear_m32_hbm_counters.md")
 
 
 def parse():
@@ -37,86 +59,145 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--kernel-reps", type=int, default=400, help="launches per per-kernel timing graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--hot", action="store_true", help="one weight copy per format (cache-resident)")
-    p.add_argument("--only", default=None, help="time only this format's kernel (profiling aid)")
     p.add_argument("--no-sweep", action="store_true", help="skip the M sweep (MXFP4 M=1..4096, static FP8 M=4096)")
+    p.add_argument("--trace-summary", metavar="DIR", help="summarize a rocprofv3 --kernel-trace directory")
+    p.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarize two rocprofv3 --pmc directories (FETCH_SIZE, WRITE_SIZE)")
+    p.add_argument("--no-hot", action="store_true", help="skip the hot (one copy) graphs, e.g. for counter runs")
+    p.add_argument("--out", help="file for the summary (default: stdout)")
+    p.add_argument("--title", default="", help="first line of the summary")
+    p.add_argument("--cmd", default="", help="the command that produced the rocprofv3 output (recorded)")
     return p.parse_args()
 
 
-def effective_bytes(fmt):
+# ------------------------------------------------------------------ byte counts
+
+
+def layout(fmt):
     from weight_only_bit_dequant_amd import wq
 
-    if fmt == "static_fp8":
-        _, pb, sb, _ = wq.wq_layout("fp8", N, K)
+    return wq.wq_layout("fp8" if fmt in ("static_fp8", "static_gemm") else fmt, N, K)
+
+
+def effective_bytes(name):
+    """Metric numerator: packed weight + scale bytes one launch streams."""
+    if name == "static_q":
+        return 0
+    _, pb, sb, gb = layout(name)
+    if name in ("static_fp8", "static_gemm"):
         return pb + sb + 4  # + the activation scale
-    _, pb, sb, gb = wq.wq_layout(fmt, N, K)
     return pb + sb + gb
 
 
-def algorithmic_bytes(fmt):
-    """Bytes one launch must move at minimum: weight stream + X + bias + Y."""
-    xb = M * K * 2
-    yb = M * N * 2
-    if fmt == "static_fp8":
-        return effective_bytes(fmt) + xb + yb  # X read once by the act-Q (fp8 copy stays on chip/L2)
-    return effective_bytes(fmt) + xb + N * 2 + yb
+def algorithmic_bytes(name):
+    """Bytes a launch must move at minimum: weight stream + activations + bias + Y."""
+    xb, yb = M * K * 2, M * N * 2
+    if name == "static_q":
+        return xb + M * K + 4              # bf16 X in, E4M3 X out, act_scale
+    if name == "static_gemm":
+        return effective_bytes(name) + M * K + yb
+    if name == "static_fp8":
+        return effective_bytes(name) + xb + yb  # the E4M3 copy of X stays in L2
+    return effective_bytes(name) + xb + N * 2 + yb
 
 
-def cpu_baseline(seconds_budget=12.0):
-    """Time the CPU oracle (dequantize + fp64 GEMM + bias) per format on the
-    full 4096x3072 layer at M=32 -- the same computation the step does."""
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """Per-kernel HBM bytes per launch from the committed counter profile, if
+    it was taken on the current kernel sources; else {}."""
+    try:
+        text = open(COUNTERS_PROFILE).read()
+    except OSError:
+        return {}
+    m = re.search(r"<!-- traffic (\{.*?\}) -->", text, re.S)
+    if not m:
+        return {}
+    rec = json.loads(m.group(1))
+    if rec.get("src_sha256") != kernel_source_hash():
+        return {}
+    return rec.get("bytes_per_launch", {})
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+
+def cpu_baseline(seconds_per_format=3.0):
+    """The CPU oracle on the step's work (dequantize + fp64 GEMM + bias per
+    weight-only format; E4M3 act Q + fp64 DQ-GEMM for static FP8) on the full
+    4096x3072 layer at M=32, with all host threads and with one."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import gemm as G
     from oracle import quant as Q
+    from oracle import static_fp8 as S
     from weight_only_bit_dequant_amd import synth
 
-    try:
-        from threadpoolctl import threadpool_info
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    cases = {}
+    quant_s = {}
+    for name in STEP:
+        info = synth.WORKLOADS[name]
+        W, b, X = synth.linear_case(N, K, M, cfg=info["cfg"], bias=info["bias"])
+        t0 = time.perf_counter()
+        if name == "static_fp8":
+            wq_, ws_ = Q.quantize_fp8_row(W)
+            cal = [synth.activations(M, K, synth.SEED_CAL + 100 + i) for i in range(10)]
+            s = S.scale_from_amax(max(S.absmax(c) for c in cal))
+            cases[name] = lambda X=X, s=s, wq_=wq_, ws_=ws_: S.static_linear_fp64(S.quantize_act(X, s), s, wq_, ws_)
+        else:
+            codes, scales, g = Q.quantize(name, W)
+            cases[name] = lambda n=name, c=codes, sc=scales, g=g, X=X, b=b: G.linear_fp64(X, Q.dequant(n, c, sc, g), b)
+        quant_s[name] = round(time.perf_counter() - t0, 3)
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    total_bytes = 0
-    total_time = 0.0
-    per = {}
-    per_fmt_budget = seconds_budget / len(FORMATS)
-    for fmt in FORMATS:
-        cfg = synth.WORKLOADS[fmt]["cfg"]
-        W, b, X = synth.linear_case(N, K, M, cfg=cfg)
-        codes, scales, g = Q.quantize(fmt, W)
+    def timed(fn, budget, min_reps):
         reps = []
-        t_fmt = time.perf_counter()
-        while len(reps) < 3 or time.perf_counter() - t_fmt < per_fmt_budget:
+        t_all = time.perf_counter()
+        while len(reps) < min_reps or time.perf_counter() - t_all < budget:
             t0 = time.perf_counter()
-            Wd = Q.dequant(fmt, codes, scales, g)
-            G.linear_fp64(X, Wd, b)
+            fn()
             reps.append(time.perf_counter() - t0)
-        t = float(np.median(reps))
-        per[fmt] = t
-        total_bytes += effective_bytes(fmt)
-        total_time += t
+        return float(np.median(reps))
+
+    per, per1 = {}, {}
+    for name, fn in cases.items():
+        per[name] = timed(fn, seconds_per_format, 3)
+        with threadpool_limits(1):
+            per1[name] = timed(fn, 0.0, 1)
+    eff = sum(effective_bytes(n) for n in STEP)
     return {
-        "value": total_bytes / total_time / 1e12,
+        "value": eff / sum(per.values()) / 1e12,
         "unit": "TB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": "full 4096x3072 layer at M=32: dequantize + fp64 GEMM + bias per weight-only format "
-                  "(INT4, FP8, NVFP4, MXFP4), repeated for ~3 s per format, median; effective weight bytes / "
-                  "oracle time",
+        "sample": "one full step on the host: the full 4096x3072 layer at M=32 for each of INT4, FP8, NVFP4, "
+                  "MXFP4 (dequantize + fp64 GEMM + bias) and static FP8 (E4M3 act Q + fp64 DQ-GEMM), median of "
+                  ">=3 runs (~3 s) per format; step effective weight bytes / summed oracle time",
         "seconds_per_format": {k: round(v, 4) for k, v in per.items()},
+        "single_thread": {"cores": 1, "value": eff / sum(per1.values()) / 1e12,
+                          "seconds_per_format": {k: round(v, 4) for k, v in per1.items()}},
+        "oracle_quantize_seconds": quant_s,
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 
 
-def m_sweep(layers, dev, capture):
-    """The other workload points (reported beside the M=32 line): MXFP4 at
+# ------------------------------------------------------------------ GPU timing
+
+
+def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
+    """The other workload points, reported beside the M=32 line: MXFP4 at
     M in {1, 32, 256, 4096} and the static-FP8 layer at M=4096, each timed as a
     graph of back-to-back launches over the same cold weight copies.  Large M
-    is bound by the matrix cores: FLOP/s against the dense bf16 (MXFP4) or
-    FP8 (static) peak."""
+    is bound by the matrix cores: FLOP/s against the dense bf16 (MXFP4) or FP8
+    (static) peak."""
     import torch
 
     from weight_only_bit_dequant_amd import synth, wq
@@ -141,7 +222,7 @@ def m_sweep(layers, dev, capture):
                     else:
                         wq.wq_linear("mxfp4", X, r["packed"], r["scales"], None, lay["bias"], N, Y, ws)
 
-            reps = 200 if Mv <= 256 else 30
+            reps = reps_small if Mv <= 256 else reps_large
             g = capture(run, reps)
             g.replay()
             torch.cuda.synchronize()
@@ -164,8 +245,7 @@ def m_sweep(layers, dev, capture):
     return res
 
 
-def main():
-    args = parse()
+def main_bench(args):
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
@@ -175,16 +255,17 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    Kst = args.steps
 
     # ---------------- data: seeded synthetic layer per format, quantized on the GPU
     layers = {}
-    for fmt in FORMATS + ["static_fp8"]:
+    for fmt in STEP:
         info = synth.WORKLOADS[fmt]
         W, b, X = synth.linear_case(N, K, M, cfg=info["cfg"], bias=info["bias"])
         qfmt = "fp8" if fmt == "static_fp8" else fmt
         q = wq.quantize(qfmt, synth.as_torch_bf16(W, dev))
         eff = effective_bytes(fmt)
-        copies = 1 if args.hot else max(2, -(-COLD_BYTES // eff))
+        copies = max(2, -(-COLD_BYTES // eff))
         reps = [{"packed": q["packed"], "scales": q["scales"], "global": q["global"]}]
         for _ in range(copies - 1):
             reps.append({"packed": q["packed"].clone(), "scales": q["scales"].clone(),
@@ -195,20 +276,31 @@ def main():
         if fmt == "static_fp8":
             cal = [synth.as_torch_bf16(synth.activations(M, K, synth.SEED_CAL + 100 + i), dev) for i in range(10)]
             lay["act_scale"], _ = wq.calibrate_act_scale(cal)
+            lay["Xq"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
         layers[fmt] = lay
     ws_bytes = max([wq.wq_linear_workspace(f, M, N, K) for f in FORMATS] + [wq.wq_fp8_static_workspace(M, N, K)])
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream_pool = torch.empty(STREAM_POOL, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(wq.wq_read_stream_words(STREAM_POOL), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
-    def launch(fmt, i):
-        lay = layers[fmt]
-        r = lay["reps"][i % len(lay["reps"])]
-        if fmt == "static_fp8":
+    def launch(name, i, hot=False):
+        lay = layers["static_fp8" if name.startswith("static") else name]
+        r = lay["reps"][0 if hot else i % len(lay["reps"])]
+        if name == "static_fp8":
             wq.wq_fp8_static_linear(lay["X"], lay["act_scale"], r["packed"], r["scales"], lay["bias"], lay["Y"], ws)
+        elif name == "static_q":
+            wq.wq_fp8_quantize_act(lay["X"], lay["act_scale"], lay["Xq"])
+        elif name == "static_gemm":
+            wq.wq_fp8_linear(lay["Xq"], lay["act_scale"], r["packed"], r["scales"], lay["bias"], lay["Y"], ws)
         else:
             wq.wq_linear(lay["fmt"], lay["X"], r["packed"], r["scales"], r["global"], lay["bias"], N, lay["Y"], ws)
 
-    step_fmts = [args.only] if args.only else FORMATS + ["static_fp8"]
+    def stream_launch(fmt, i):
+        size = -(-effective_bytes(fmt) // 256) * 256
+        slots = STREAM_POOL // size
+        off = (i % slots) * size
+        wq.wq_read_stream(stream_pool[off:off + size], sink, effective_bytes(fmt) // 16 * 16)
 
     def capture(fn, count):
         g = torch.cuda.CUDAGraph()
@@ -225,66 +317,88 @@ def main():
 
     def steps_fn(first, count):
         for st in range(first, first + count):
-            for f in step_fmts:
+            for f in STEP:
                 launch(f, st)
 
-    # ---------------- whole-step timing
+    # ---------------- graphs: the step, each single kernel, the stream ceiling, the hot case
+    parts = [("step", capture(steps_fn, Kst))]
+    for k in KERNELS:
+        parts.append((k, capture(lambda a, c, k=k: [launch(k, i) for i in range(a, a + c)], Kst)))
+    for f in STEP:
+        parts.append(("stream_" + f, capture(lambda a, c, f=f: [stream_launch(f, i) for i in range(a, a + c)], Kst)))
+    for f in ([] if args.no_hot else FORMATS):
+        parts.append(("hot_" + f, capture(lambda a, c, f=f: [launch(f, i, hot=True) for i in range(a, a + c)], Kst)))
     g_warm = capture(steps_fn, max(1, args.warmup))
-    g_timed = capture(steps_fn, args.steps)
     g_warm.replay()
+    for _, g in parts[1:]:
+        g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # ---------------- timed region
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    e0.record()
-    g_timed.replay()
-    e1.record()
+    ev[0].record()
+    for i, (_, g) in enumerate(parts):
+        g.replay()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / args.steps
-    step_eff = sum(effective_bytes(f) for f in step_fmts)
+    us = {name: ev[i].elapsed_time(ev[i + 1]) * 1e3 / Kst for i, (name, _) in enumerate(parts)}
+    ms_per_step = us["step"] / 1e3
+    step_eff = sum(effective_bytes(f) for f in STEP)
     value = step_eff / (ms_per_step * 1e-3) / 1e12
 
-    # ---------------- per-kernel timing (back-to-back launches of one kernel)
+    traffic = committed_traffic()
+    per_kernel = {}
+    for k in KERNELS:
+        eff, alg = effective_bytes(k), algorithmic_bytes(k)
+        d = {"us_per_launch": round(us[k], 3), "algorithmic_bytes": alg,
+             "algorithmic_GBps": round(alg / (us[k] * 1e-6) / 1e9, 1)}
+        if eff:
+            d.update({"effective_bytes": eff, "effective_TBps": round(eff / (us[k] * 1e-6) / 1e12, 4),
+                      "pct_hbm_peak": round(100.0 * eff / (us[k] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)})
+        if k in FORMATS:
+            d["copies"] = len(layers[k]["reps"])
+            if "hot_" + k in us:
+                d["hot_us_per_launch"] = round(us["hot_" + k], 3)
+        if k == "static_gemm":
+            d["copies"] = len(layers["static_fp8"]["reps"])
+        if k in traffic:
+            d["traffic_bytes"] = traffic[k]
+        per_kernel[k] = d
     per_format = {}
-    for f in step_fmts:
-        g = capture(lambda first, count, f=f: [launch(f, i) for i in range(first, first + count)], args.kernel_reps)
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / args.kernel_reps
+    for f in STEP:
         eff = effective_bytes(f)
+        if f == "static_fp8":
+            t = us["static_q"] + us["static_gemm"]
+        else:
+            t = us[f]
         per_format[f] = {
-            "us_per_launch": round(us, 3),
-            "effective_TBps": round(eff / (us * 1e-6) / 1e12, 4),
-            "pct_hbm_peak": round(100.0 * eff / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-            "effective_bytes": eff,
-            "algorithmic_bytes": algorithmic_bytes(f),
-            "copies": len(layers[f]["reps"]),
+            "us_per_launch": round(t, 3),
+            "effective_TBps": round(eff / (t * 1e-6) / 1e12, 4),
+            "pct_hbm_peak": round(100.0 * eff / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "stream_ceiling_us": round(us["stream_" + f], 3),
+            "pct_of_stream_ceiling": round(100.0 * us["stream_" + f] / t, 1),
             "launches": 2 if f == "static_fp8" else 1,
         }
-        del g
 
-    sweep = None if (args.no_sweep or args.only) else m_sweep(layers, dev, capture)
-
-    dominant = max(per_format, key=lambda f: per_format[f]["us_per_launch"])
-    d = per_format[dominant]
-    achieved = d["algorithmic_bytes"] / (d["us_per_launch"] * 1e-6) / 1e9
+    dominant = max(KERNELS, key=lambda k: us[k])
+    d = per_kernel[dominant]
+    achieved = d["algorithmic_bytes"] / (us[dominant] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dominant,
-                "algorithmic_bytes_per_launch": d["algorithmic_bytes"]}
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic.get(dominant), "kernel": dominant,
+                "algorithmic_bytes_per_launch": d["algorithmic_bytes"], "us_per_launch": d["us_per_launch"]}
+
+    sweep = None if args.no_sweep else m_sweep(layers, dev, capture)
 
     out = {
         "metric": METRIC,
         "value": round(value, 4),
         "unit": "TB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": Kst,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
@@ -294,9 +408,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "nn.Linear(3072->4096) bf16+bias, M=32: INT4-g128 / FP8-row / NVFP4 / MXFP4 "
                                "weight-only dequant-GEMMs + static-FP8 (act Q + FP8 GEMM), cold weight copies",
-                   "M": M, "N": N, "K": K, "formats": step_fmts, "cold": not args.hot},
+                   "M": M, "N": N, "K": K, "formats": STEP, "cold": True},
         "roofline": roofline,
         "per_format": per_format,
+        "per_kernel": per_kernel,
+        "kernel_source_sha256": kernel_source_hash(),
         "wall_s_timed": round(t_wall, 4),
     }
     if sweep is not None:
@@ -304,6 +420,109 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
+
+
+# ------------------------------------------------------------------ rocprofv3 summaries
+
+KERNEL_LABELS = {1: "int4", 2: "fp8", 3: "nvfp4", 4: "mxfp4", 5: "static_gemm"}
+
+
+def label_of(name):
+    """Step label of a kernel name in an M=32 run (`--no-sweep`), else None."""
+    m = re.search(r"k_linear<(\d+), ", name)
+    if m:
+        return KERNEL_LABELS.get(int(m.group(1)))
+    if "k_quant_act" in name:
+        return "static_q"
+    if "k_read_stream" in name:
+        return "stream"
+    return None
+
+
+def _rows(d, suffix):
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, d))
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short(name, n=90):
+    return name if len(name) <= n else name[:n]
+
+
+def trace_summary(d, cmd):
+    import numpy as np
+
+    rows = _rows(d, "kernel_trace.csv")
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | calls | avg µs | p10 | p50 | p90 | min | max |", "|---|---|---|---|---|---|---|---|"]
+    for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        a = np.asarray(v)
+        lines.append("| `%s` | %d | %.3f | %.3f | %.3f | %.3f | %.3f | %.3f |" % (
+            _short(name), len(a), a.mean(), np.percentile(a, 10), np.percentile(a, 50), np.percentile(a, 90),
+            a.min(), a.max()))
+    return "Command (from /tmp with TMPDIR=/tmp, repo at $R):\n\n```\n%s\n```\n\n%s\n" % (cmd, "\n".join(lines))
+
+
+def counters_summary(fetch_dir, write_dir, cmd):
+    import numpy as np
+
+    out = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for r in _rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            out.setdefault((r["Kernel_Name"], cname), []).append(float(r["Counter_Value"]))
+    # calibration: the FP8 pack is a plain 16-byte copy of N*K bytes
+    copy_bytes = N * K
+    cal = {}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = [x for (n, c), xs in out.items() if c == cname and "k_copy16" in n for x in xs]
+        if not v:
+            raise SystemExit("no k_copy16 dispatch for %s calibration" % cname)
+        cal[cname] = copy_bytes / (float(np.mean(v)) * 1024.0)
+    per = {}
+    lines = ["| kernel | label | counter | dispatches | mean KiB / dispatch | scaled bytes / dispatch |",
+             "|---|---|---|---|---|---|"]
+    for (name, cname), xs in sorted(out.items()):
+        kib = float(np.mean(xs))
+        scaled = kib * 1024.0 * cal[cname]
+        lab = label_of(name)
+        lines.append("| `%s` | %s | %s | %d | %.1f | %.0f |" % (_short(name, 70), lab or "", cname, len(xs), kib, scaled))
+        if lab and lab != "stream":
+            per.setdefault(lab, 0.0)
+            per[lab] += scaled
+    rec = {"src_sha256": kernel_source_hash(), "calibration": {k: round(v, 4) for k, v in cal.items()},
+           "bytes_per_launch": {k: int(round(v)) for k, v in per.items()}}
+    text = ("Commands (each counter in its own run; from /tmp with TMPDIR=/tmp, repo at $R):\n\n```\n%s\n```\n\n"
+            "Calibration: `k_copy16` (the FP8 pack, a plain 16-byte copy of N*K = %d bytes) reads and writes %d "
+            "bytes; FETCH_SIZE x %.4f and WRITE_SIZE x %.4f give bytes.  Per-launch HBM traffic (FETCH + WRITE, "
+            "scaled): %s.\n\n%s\n\n<!-- traffic %s -->\n" % (
+                cmd, copy_bytes, copy_bytes, cal["FETCH_SIZE"], cal["WRITE_SIZE"],
+                ", ".join("%s %d B" % kv for kv in sorted(rec["bytes_per_launch"].items())), "\n".join(lines),
+                json.dumps(rec)))
+    return text
+
+
+def main():
+    args = parse()
+    if args.trace_summary or args.counters_summary:
+        if args.trace_summary:
+            text = trace_summary(args.trace_summary, args.cmd)
+        else:
+            text = counters_summary(args.counters_summary[0], args.counters_summary[1], args.cmd)
+        if args.title:
+            text = "# %s\n\n%s" % (args.title, text)
+        if args.out:
+            with open(args.out, "w") as fh:
+                fh.write(text)
+        else:
+            print(text)
+        return
+    main_bench(args)
 
 
 if __name__ == "__main__":

@@ -197,6 +197,31 @@ wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float*
                                const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * The FP8 x FP8 GEMM of the static path on activations that are already
+ * quantized (same page, "Graph after export": the Q node's E4M3 output and the
+ * E4M3 weight each pass a DQ into the linear; intro: that pair runs as one FP8
+ * GEMM): Y = bf16(sum_k dec(Xq[m][k]) dec(Wq[n][k]) * act_scale * w_scale[n]
+ * (+ bias[n])).  Xq: E4M3 codes uint8 [M][K] (wq_fp8_quantize_act output, or
+ * any E4M3 tensor quantized with act_scale).  wq_fp8_static_linear is
+ * wq_fp8_quantize_act followed by this call.  K % 16 == 0.  Workspace:
+ * wq_fp8_linear_workspace bytes (0 for most shapes).
+ */
+size_t wq_fp8_linear_workspace(int64_t M, int64_t N, int64_t K);
+wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_scale, const void* Wq,
+                        const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement aid (not part of the method): reads `bytes` bytes at `p` with
+ * 16-byte vector loads, as the plain read-only stream that a weight stream of
+ * the same size is compared against.  sink[b] (device, wq_read_stream_words
+ * entries) receives the XOR of the 32-bit words of the b-th 16 KiB block, so
+ * every byte read reaches the output.  p 16-byte aligned, bytes % 16 == 0.
+ */
+size_t wq_read_stream_words(size_t bytes);
+wq_status wq_read_stream(const void* p, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

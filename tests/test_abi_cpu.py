@@ -106,6 +106,18 @@ def test_quantize_pack_dequant_validation():
                                   None) == wq.EWORKSPACE
     assert L.wq_absmax(None, 10, v(16), None) == wq.EINVAL
     assert L.wq_absmax(None, 0, None, None) == wq.OK
+    # FP8 GEMM on pre-quantized activations
+    assert L.wq_fp8_linear(v(16), 4, 24, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.EUNSUPPORTED
+    assert L.wq_fp8_linear(v(16), 4, 32, None, v(16), v(16), None, 16, v(16), None, 0, None) == wq.EINVAL
+    assert L.wq_fp8_linear(v(8), 4, 32, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.EALIGN
+    assert L.wq_fp8_linear(v(16), 0, 32, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.OK
+    assert L.wq_fp8_linear(v(16), 32, 3072, v(16), v(16), v(16), None, 256, v(16), None, 0,
+                           None) == wq.EWORKSPACE  # narrow layer: split K
+    # read-only stream (measurement aid)
+    assert L.wq_read_stream(v(16), 0, None, None) == wq.OK
+    assert L.wq_read_stream(None, 64, v(16), None) == wq.EINVAL
+    assert L.wq_read_stream(v(8), 64, v(16), None) == wq.EALIGN
+    assert L.wq_read_stream(v(16), 40, v(16), None) == wq.EUNSUPPORTED
 
 
 def test_workspace_plans_are_consistent():
@@ -116,6 +128,9 @@ def test_workspace_plans_are_consistent():
     M, N, K = 32, 4096, 3072
     gemm = wq.wq_linear_workspace("fp8", M, N, K)
     assert wq.wq_fp8_static_workspace(M, N, K) >= gemm + M * K
+    assert wq.wq_fp8_linear_workspace(M, N, K) == 0
+    assert wq.wq_fp8_linear_workspace(32, 256, 3072) > 0
+    assert wq.wq_fp8_static_workspace(32, 256, 3072) >= wq.wq_fp8_linear_workspace(32, 256, 3072) + 32 * 3072
     # wide layers have enough workgroups without K splits
     assert wq.wq_linear_workspace("mxfp4", 4096, 4096, 3072) == 0
     assert wq.wq_linear_workspace("int4", 32, 4096, 3072) == 0

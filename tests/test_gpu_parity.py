@@ -283,6 +283,51 @@ def test_static_large_layer(M):
     assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"static 3072->4096 M={M}")
 
 
+@pytest.mark.parametrize("M,N,K,bias", [(32, 4096, 3072, False), (17, 200, 512, True), (64, 256, 1024, True)])
+def test_fp8_linear_on_prequantized_activations(M, N, K, bias):
+    """wq_fp8_quantize_act then wq_fp8_linear equals wq_fp8_static_linear bit
+    for bit (same kernels) and the oracle's fp64 DQ-GEMM within the bar."""
+    W, b, X = synth.linear_case(N, K, M, cfg=70 + M)
+    b = b if bias else None
+    cal = synth.activations(32, K, synth.SEED_CAL + 300)
+    print(f"[case] fp8_linear M={M} N={N} K={K} bias={bias}", flush=True)
+    scale, _ = wq.calibrate_act_scale([dev_bf16(cal)])
+    q = wq.quantize("fp8", dev_bf16(W))
+    Xd = dev_bf16(X)
+    bd = dev_bf16(b) if b is not None else None
+    Xq = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    wq.wq_fp8_quantize_act(Xd, scale, Xq)
+    Y1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(1, wq.wq_fp8_linear_workspace(M, N, K)), dtype=torch.uint8, device=DEV)
+    wq.wq_fp8_linear(Xq, scale, q["codes"], q["scales"], bd, Y1, ws)
+    Y2 = wq.static_fp8_linear(Xd, scale, q["codes"], q["scales"], bd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    s_ref = S.scale_from_amax(S.absmax(cal))
+    wq_ref, ws_ref = Q.quantize_fp8_row(W)
+    xq_ref = S.quantize_act(X, s_ref)
+    assert np.array_equal(host(Xq), xq_ref)
+    assert_close(Y1, S.static_linear_fp64(xq_ref, s_ref, wq_ref, ws_ref, b), f"fp8_linear M={M} N={N}")
+
+
+@pytest.mark.parametrize("nbytes", [16, 1040, 16384 + 48, 4096 * 1536])
+def test_read_stream_xor(nbytes):
+    """The measurement stream reads every byte: each block's XOR equals the host's."""
+    rng = np.random.default_rng(nbytes)
+    host_words = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    print(f"[case] read_stream bytes={nbytes}", flush=True)
+    buf = torch.from_numpy(host_words.view(np.int32)).to(DEV)
+    nw = wq.wq_read_stream_words(nbytes)
+    assert nw == -(-nbytes // 16384)
+    sink = torch.full((nw + 1,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    wq.wq_read_stream(buf, sink)
+    torch.cuda.synchronize()
+    got = host(sink).view(np.uint32)
+    for blk in range(nw):
+        assert got[blk] == np.bitwise_xor.reduce(host_words[blk * 4096:(blk + 1) * 4096]), blk
+    assert got[nw] == 0x5A5A5A5A  # nothing written past the last block
+
+
 def test_workspace_reuse_across_plans():
     """Calls with different launch plans (K split across workgroups or not)
     share one cached workspace and run back to back."""

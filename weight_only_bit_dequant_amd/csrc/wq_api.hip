@@ -280,4 +280,31 @@ wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float*
                        workspace_bytes, stream);
 }
 
+size_t wq_fp8_linear_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return wq::plan_linear(wq::KF_FP8S, M, N, K).ws_bytes;
+}
+
+wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_scale, const void* Wq,
+                        const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
+  if (M == 0 || N == 0) return ok();
+  if (K > 0 && K % 16) return fail(WQ_EUNSUPPORTED, "FP8 linear needs K %% 16 == 0 (K=%lld)", (long long)K);
+  if (!Xq || !act_scale || !Wq || !w_scale || !Y) return fail(WQ_EINVAL, "wq_fp8_linear: null pointer");
+  return linear_common(wq::KF_FP8S, WQ_FP8, Xq, M, K, Wq, w_scale, nullptr, act_scale, bias, N, Y, workspace,
+                       workspace_bytes, stream);
+}
+
+size_t wq_read_stream_words(size_t bytes) { return (bytes + 16383) / 16384; }
+
+wq_status wq_read_stream(const void* p, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return ok();
+  if (!p || !sink) return fail(WQ_EINVAL, "wq_read_stream: null pointer");
+  if (!aligned16(p)) return fail(WQ_EALIGN, "wq_read_stream: p must be 16-byte aligned");
+  if (bytes % 16) return fail(WQ_EUNSUPPORTED, "wq_read_stream: bytes %% 16 != 0");
+  if (bytes >= (size_t)kMaxBufferBytes) return fail(WQ_EUNSUPPORTED, "wq_read_stream: 2^31 bytes or more");
+  return hip_status(wq::launch_read_stream(p, bytes, sink, (hipStream_t)stream), "wq_read_stream launch");
+}
+
 }  // extern "C"

@@ -58,6 +58,7 @@ hipError_t launch_gemm_tiled(int kfmt, const LinearArgs& a, const LinearPlan& p,
 
 hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t N, int64_t K, void* codes, void* scales,
                            float* gscale, hipStream_t s);
+hipError_t launch_read_stream(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_pack(int fmt, const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
 hipError_t launch_dequantize(int fmt, const void* packed, const void* scales, const float* gscale, int64_t N,
                              int64_t K, uint16_t* out, hipStream_t s);

@@ -7,6 +7,7 @@
 // scales are bit-identical to an IEEE reference.
 #include "wq_device.hpp"
 #include "wq_internal.hpp"
+#include "wq_kernel_common.hpp"
 
 namespace wq {
 
@@ -365,6 +366,37 @@ hipError_t launch_fp8_scale(const float* amax, float* scale, int64_t count, hipS
 hipError_t launch_quantize_act(const uint16_t* X, int64_t numel, const float* act_scale, uint8_t* Xq,
                                hipStream_t s) {
   k_quant_act<<<grid_for(numel / 8 + 1), kThreads, 0, s>>>(X, numel, act_scale, Xq);
+  return hipGetLastError();
+}
+
+// Read-only stream (measurement aid): workgroup b reads the 16 KiB block b
+// (1024 chunks of 16 bytes, four per thread, all issued before the first use)
+// and stores the XOR of its 32-bit words to sink[b].  Offsets past the end
+// read zero (neutral for XOR).  One plain store per workgroup: no atomics on a
+// shared address, which would serialize the workgroups.
+namespace {
+__global__ __launch_bounds__(256) void k_read_stream(const void* p, uint32_t bytes, uint32_t* sink) {
+  __shared__ uint32_t part[4];
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(p, bytes);
+  const uint32_t base = (uint32_t)blockIdx.x * 1024u + threadIdx.x;
+  u32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = bload128(r, (base + 256u * q) * 16u);
+  uint32_t h = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) h ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) h ^= __shfl_xor(h, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = h;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+}  // namespace
+
+hipError_t launch_read_stream(const void* p, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t chunks = bytes / 16;
+  const unsigned grid = (unsigned)((chunks + 1023) / 1024);
+  k_read_stream<<<grid, 256, 0, s>>>(p, (uint32_t)bytes, sink);
   return hipGetLastError();
 }
 

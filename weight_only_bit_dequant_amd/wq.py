@@ -61,8 +61,15 @@ def lib():
         L.wq_fp8_static_workspace.argtypes = [I64, I64, I64]
         L.wq_fp8_static_workspace.restype = SZ
         L.wq_fp8_static_linear.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, SZ, P]
+        L.wq_fp8_linear_workspace.argtypes = [I64, I64, I64]
+        L.wq_fp8_linear_workspace.restype = SZ
+        L.wq_fp8_linear.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, SZ, P]
+        L.wq_read_stream.argtypes = [P, SZ, P, P]
+        L.wq_read_stream_words.argtypes = [SZ]
+        L.wq_read_stream_words.restype = SZ
         for name in ("wq_layout", "wq_quantize", "wq_pack", "wq_dequantize", "wq_linear", "wq_absmax",
-                     "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear"):
+                     "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear", "wq_fp8_linear",
+                     "wq_read_stream"):
             getattr(L, name).restype = I
         if L.wq_abi_version() != 1:
             raise RuntimeError("libwq ABI version mismatch")
@@ -159,14 +166,35 @@ def wq_fp8_static_linear(X, act_scale, Wq, w_scale, bias, Y, workspace):
            "wq_fp8_static_linear")
 
 
+def wq_fp8_linear_workspace(M, N, K):
+    return lib().wq_fp8_linear_workspace(M, N, K)
+
+
+def wq_fp8_linear(Xq, act_scale, Wq, w_scale, bias, Y, workspace=None):
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().wq_fp8_linear(_ptr(Xq), M, K, _ptr(act_scale), _ptr(Wq), _ptr(w_scale), _ptr(bias), N, _ptr(Y),
+                               _ptr(workspace), ws_bytes, _stream(Xq.device)), "wq_fp8_linear")
+
+
+def wq_read_stream_words(nbytes):
+    return lib().wq_read_stream_words(nbytes)
+
+
+def wq_read_stream(buf, sink, nbytes=None):
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(lib().wq_read_stream(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)), "wq_read_stream")
+
+
 # ---------------------------------------------------------------- helpers: allocation + chaining
 
 _WS = {}
 
 
 def workspace(nbytes, device):
-    """A zero-filled uint8 workspace of at least `nbytes`, cached per (device,
-    stream).  The kernels leave their counters at zero, so it is reused."""
+    """A uint8 workspace of at least `nbytes`, cached per (device, stream).
+    It holds split-K partials, which need no initialisation, so it is reused."""
     if nbytes == 0:
         return None
     dev = torch.device(device)
