@@ -64,6 +64,7 @@ def parse():
     p.add_argument("--trace-summary", metavar="DIR", help="summarize a rocprofv3 --kernel-trace directory")
     p.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarize two rocprofv3 --pmc directories (FETCH_SIZE, WRITE_SIZE)")
+    p.add_argument("--sweep-only", action="store_true", help="only the M sweep (e.g. for counter runs at large M)")
     p.add_argument("--no-hot", action="store_true", help="skip the hot (one copy) graphs, e.g. for counter runs")
     p.add_argument("--out", help="file for the summary (default: stdout)")
     p.add_argument("--title", default="", help="first line of the summary")
@@ -259,7 +260,7 @@ def main_bench(args):
 
     # ---------------- data: seeded synthetic layer per format, quantized on the GPU
     layers = {}
-    for fmt in STEP:
+    for fmt in (["mxfp4", "static_fp8"] if args.sweep_only else STEP):
         info = synth.WORKLOADS[fmt]
         W, b, X = synth.linear_case(N, K, M, cfg=info["cfg"], bias=info["bias"])
         qfmt = "fp8" if fmt == "static_fp8" else fmt
@@ -278,6 +279,17 @@ def main_bench(args):
             lay["act_scale"], _ = wq.calibrate_act_scale(cal)
             lay["Xq"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
         layers[fmt] = lay
+    if args.sweep_only:
+        def capture_only(fn, count):
+            g = torch.cuda.CUDAGraph()
+            fn(0, 1)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                fn(1, count)
+            torch.cuda.synchronize()
+            return g
+        print(json.dumps({"m_sweep": m_sweep(layers, dev, capture_only, reps_small=20, reps_large=5)}))
+        return
     ws_bytes = max([wq.wq_linear_workspace(f, M, N, K) for f in FORMATS] + [wq.wq_fp8_static_workspace(M, N, K)])
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream_pool = torch.empty(STREAM_POOL, dtype=torch.uint8, device=dev)

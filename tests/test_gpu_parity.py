@@ -175,6 +175,22 @@ def test_linear_mxfp4_m_sweep(M):
         assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"mxfp4 M={M} sampled rows")
 
 
+# (M, N, K) -> tiled workgroup shape / K groups chosen by the plan:
+#   64x64 tiles in 4 K groups with uneven group ranges (34 steps), 64x64 in 2,
+#   128x64 in 2, 64x128 in 2 (ragged N), ragged M in 4 groups
+TILED_CASES = [(256, 1024, 2176), (640, 2048, 1152), (384, 4096, 1024), (6144, 192, 1024), (200, 1024, 2048)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K", TILED_CASES)
+def test_linear_tiled_k_groups(fmt, M, N, K):
+    W, b, X = synth.linear_case(N, K, M, cfg=80 + M % 7)
+    _, Y = run_linear(fmt, W, b, X)
+    rows = np.arange(M) if M <= 1024 else np.arange(0, M, 37)
+    ref = oracle_linear(fmt, W, b, X[rows])
+    assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"{fmt} tiled M={M} N={N} K={K}")
+
+
 def test_linear_dense_bf16():
     W, b, X = synth.linear_case(4096, 3072, 32, cfg=6)
     print("[case] dense bf16 linear", flush=True)
@@ -283,7 +299,8 @@ def test_static_large_layer(M):
     assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"static 3072->4096 M={M}")
 
 
-@pytest.mark.parametrize("M,N,K,bias", [(32, 4096, 3072, False), (17, 200, 512, True), (64, 256, 1024, True)])
+@pytest.mark.parametrize("M,N,K,bias", [(32, 4096, 3072, False), (17, 200, 512, True), (64, 256, 1024, True),
+                                        (256, 4096, 3072, False), (640, 2048, 1152, True)])
 def test_fp8_linear_on_prequantized_activations(M, N, K, bias):
     """wq_fp8_quantize_act then wq_fp8_linear equals wq_fp8_static_linear bit
     for bit (same kernels) and the oracle's fp64 DQ-GEMM within the bar."""

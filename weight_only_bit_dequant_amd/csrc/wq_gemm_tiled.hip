@@ -8,8 +8,8 @@
 //    latency overlaps the current step's matrix-core work;
 //  * the weight chunk is decoded once per workgroup into bf16 (E4M3 for the
 //    static path) and written to LDS next to the activation tile (double
-//    buffered, rows padded by 16 bytes so the operand reads hit distinct
-//    banks);
+//    buffered; the 16-byte chunks of each row are XOR-swizzled with row bits
+//    so that operand reads and tile writes are free of bank conflicts);
 //  * each wave reads 16x32 operand fragments from LDS and issues
 //    v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x32_fp8_fp8 for static FP8).
 // Decode: FP8 weights, NVFP4 (E2M1 x E4M3 block scale) and MXFP4 (E2M1 x
@@ -41,8 +41,19 @@ struct TileFmt {
   static constexpr int OB = ACT8 ? 1 : 2;  // bytes per weight operand element in LDS
   // packed weight bytes per column per step
   static constexpr int WSTEP = (F == KF_BF16) ? 128 : ((F == KF_FP8 || F == KF_FP8S) ? 64 : 32);
-  static constexpr int ARS = kBK * XB + 16;  // padded LDS row strides
-  static constexpr int BRS = kBK * OB + 16;
+  static constexpr int ARS = kBK * XB;  // LDS row strides (bytes)
+  static constexpr int BRS = kBK * OB;
+  static_assert(ARS == BRS, "activation and weight rows share one swizzle");
+  // Position of 16-byte chunk k in LDS row r.  Rows of 8 chunks (bf16) XOR
+  // the chunk index with r & 7, rows of 4 chunks (E4M3) with (r >> 1) & 3:
+  // with these, a quarter-wave reading one chunk from each of 16 rows, and a
+  // wave writing whole rows, hit every LDS bank once (measured with the
+  // SQ_LDS_BANK_CONFLICT counter on gfx950; padding rows by 16 bytes instead
+  // doubles the read cycles).
+  __device__ static __forceinline__ int pos(int r, int k) {
+    if constexpr (ARS == 128) return k ^ (r & 7);
+    else return k ^ ((r >> 1) & 3);
+  }
 };
 
 template <int F, int BM, int BN>
@@ -51,9 +62,12 @@ constexpr int tile_smem() {
 }
 
 // Decode one 16-byte packed chunk of a weight column into operand bytes in
-// LDS (`sc` holds the chunk's scale codes).
+// LDS: `row` is the column's LDS row, k0 the index of its first 16-byte output
+// chunk in that row (`sc` holds the chunk's scale codes).
 template <int F>
-__device__ __forceinline__ void decode_store(unsigned char* dst, u32x4 w, uint32_t sc) {
+__device__ __forceinline__ void decode_store(unsigned char* row, int r, int k0, u32x4 w, uint32_t sc) {
+  using TF = TileFmt<F>;
+  auto at = [&](int p) { return reinterpret_cast<bf16x8*>(row + TF::pos(r, k0 + p) * 16); };
   if constexpr (F == KF_INT4) {
     const float s = bitsf(sc << 16);
 #pragma unroll
@@ -61,28 +75,28 @@ __device__ __forceinline__ void decode_store(unsigned char* dst, u32x4 w, uint32
       // 8 nibbles -> bf16(code * s), K order kept
       const bf16x8 biased = dec_int4_biased(w[j]);  // 136 + code, exact
       const u32x4 bb = __builtin_bit_cast(u32x4, biased);
-      bf16x8 r;
+      bf16x8 r8;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const float lo = bitsf(bb[p] << 16), hi = bitsf(bb[p] & 0xFFFF0000u);
-        r[2 * p] = (__bf16)fmaf(lo, s, -136.f * s);
-        r[2 * p + 1] = (__bf16)fmaf(hi, s, -136.f * s);
+        r8[2 * p] = (__bf16)fmaf(lo, s, -136.f * s);
+        r8[2 * p + 1] = (__bf16)fmaf(hi, s, -136.f * s);
       }
-      *reinterpret_cast<bf16x8*>(dst + 16 * j) = r;
+      *at(j) = r8;
     }
   } else if constexpr (F == KF_NVFP4) {
     const float d0 = e4m3_decode(sc & 0xFFu), d1 = e4m3_decode((sc >> 8) & 0xFFu);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(dst + 16 * j) = dec_fp4_mul(w[j], j < 2 ? d0 : d1);
+    for (int j = 0; j < 4; ++j) *at(j) = dec_fp4_mul(w[j], j < 2 ? d0 : d1);
   } else if constexpr (F == KF_MXFP4) {
     const float p = e8m0_decode(sc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(dst + 16 * j) = dec_fp4_pow2(w[j], p);
+    for (int j = 0; j < 4; ++j) *at(j) = dec_fp4_pow2(w[j], p);
   } else if constexpr (F == KF_FP8) {
-    *reinterpret_cast<bf16x8*>(dst) = dec_fp8(w[0], w[1]);
-    *reinterpret_cast<bf16x8*>(dst + 16) = dec_fp8(w[2], w[3]);
+    *at(0) = dec_fp8(w[0], w[1]);
+    *at(1) = dec_fp8(w[2], w[3]);
   } else {  // BF16 weights and E4M3 weights of the static path are stored as they are
-    *reinterpret_cast<u32x4*>(dst) = w;
+    *reinterpret_cast<u32x4*>(at(0)) = w;
   }
 }
 
@@ -92,8 +106,8 @@ constexpr int decoded_bytes() {
   return (F == KF_INT4 || F == KF_NVFP4 || F == KF_MXFP4) ? 64 : ((F == KF_FP8) ? 32 : 16);
 }
 
-template <int F, int BM, int BN, int STG>
-__global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
+template <int F, int BM, int BN, int STG, int KS>
+__global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
   using TF = TileFmt<F>;
   constexpr int TM = BM / 32, TN = BN / 32;  // 16x16 tiles per wave (waves 2 x 2)
   constexpr int LA = kBK * TF::XB / 16;       // 16-byte chunks per activation row per step
@@ -104,10 +118,15 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
   constexpr int DB = decoded_bytes<F>();
   static_assert(NA * 256 == BM * LA, "activation tile must split evenly over 256 threads");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* As = smem;                         // [2][BM][ARS]
-  unsigned char* Bs = smem + 2 * BM * TF::ARS;      // [2][BN][BRS]
+  // KS groups of 4 waves split K inside the workgroup: group kg owns a
+  // contiguous range of K steps and its own double-buffered tiles; all groups
+  // step in lockstep (one workgroup barrier per step) and are summed through
+  // LDS at the end.
+  const int kg = (int)threadIdx.x >> 8;
+  unsigned char* As = smem + kg * tile_smem<F, BM, BN>();  // [2][BM][ARS]
+  unsigned char* Bs = As + 2 * BM * TF::ARS;                // [2][BN][BRS]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
   const int M = a.M, N = a.N, K = a.K;
@@ -133,6 +152,9 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
   const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
 
   const int KT = (K + kBK - 1) / kBK;
+  const int KTg = (KT + KS - 1) / KS;  // steps per group
+  const int kbeg = kg * KTg * kBK;     // this group's K range [kbeg, kend)
+  const int kend = min(K, kbeg + KTg * kBK);
 
   // STG register stages of global loads are in flight: the loads of step k
   // live in stage k % STG from the moment they are issued (STG steps ahead)
@@ -145,8 +167,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
       const int row = q * (256 / LA) + tid / LA;
-      const int kx = kt * kBK + (tid % LA) * (16 / TF::XB);
-      xa[q] = bload128(Xr, off_if(kx < K, ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)kx) * (uint32_t)TF::XB));
+      const int kx = kbeg + kt * kBK + (tid % LA) * (16 / TF::XB);
+      xa[q] = bload128(Xr, off_if(kx < kend, ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)kx) * (uint32_t)TF::XB));
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
@@ -157,8 +179,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
       const uint32_t n = (uint32_t)(n0 + col);
       // K elements per 16-byte chunk: 4-bit 32, FP8 16, BF16 8; k0 is the chunk's first K
       const int kpc = (F == KF_BF16) ? 8 : ((F == KF_FP8 || F == KF_FP8S) ? 16 : 32);
-      const int k0 = kt * kBK + part * kpc;
-      const bool ok = k0 < K;
+      const int k0 = kbeg + kt * kBK + part * kpc;
+      const bool ok = k0 < kend;
       const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : ((F == KF_FP8 || F == KF_FP8S) ? (uint32_t)k0 : (uint32_t)k0 / 2u);
       wb[q] = bload128(Wr, off_if(ok, n * wrow + byte0));
       if constexpr (F == KF_INT4) sb[q] = bload16(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u));
@@ -173,13 +195,13 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
       const int row = q * (256 / LA) + tid / LA;
-      *reinterpret_cast<u32x4*>(A + row * TF::ARS + (tid % LA) * 16) = xa[q];
+      *reinterpret_cast<u32x4*>(A + row * TF::ARS + TF::pos(row, tid % LA) * 16) = xa[q];
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
       const int id = (q * 256 + tid) % CB;
       const int col = id / LB, part = id % LB;
-      decode_store<F>(B + col * TF::BRS + part * DB, wb[q], sb[q]);
+      decode_store<F>(B + col * TF::BRS, col, part * (DB / 16), wb[q], sb[q]);
     }
   };
 
@@ -201,28 +223,43 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
   auto compute = [&](int buf) {
     const unsigned char* A = As + buf * BM * TF::ARS;
     const unsigned char* B = Bs + buf * BN * TF::BRS;
+    if constexpr (TF::ACT8) {
+      // E4M3: lane (g, c) reads the 16-byte chunk g of its rows, i.e. K
+      // 16g .. 16g+15 of the step, and feeds its two halves to the two MFMAs
+      // (K 16g + 8kk .. +7 in MFMA kk; the same K order on both operands)
+      u32x4 af[TM], bf[TN];
 #pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      if constexpr (TF::ACT8) {
-        u32x2 af[TM], bf[TN];
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + 16 * i + c;
+        af[i] = *reinterpret_cast<const u32x4*>(A + r * TF::ARS + TF::pos(r, g) * 16);
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * (BN / 2) + 16 * t + c;
+        bf[t] = *reinterpret_cast<const u32x4*>(B + r * TF::BRS + TF::pos(r, g) * 16);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const u32x2*>(A + (wm * (BM / 2) + 16 * i + c) * TF::ARS + (kk * 32 + 8 * g));
 #pragma unroll
-        for (int t = 0; t < TN; ++t)
-          bf[t] = *reinterpret_cast<const u32x2*>(B + (wn * (BN / 2) + 16 * t + c) * TF::BRS + (kk * 32 + 8 * g));
+          for (int t = 0; t < TN; ++t)
+            acc[i][t] = mfma_fp8(af[i][2 * kk], af[i][2 * kk + 1], bf[t][2 * kk], bf[t][2 * kk + 1], acc[i][t]);
+    } else {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int t = 0; t < TN; ++t) acc[i][t] = mfma_fp8(af[i].x, af[i].y, bf[t].x, bf[t].y, acc[i][t]);
-      } else {
+      for (int kk = 0; kk < kBK / 32; ++kk) {
+        // lane (g, c): K 32kk + 8g .. +7 of the step = 16-byte chunk 4kk + g
         bf16x8 af[TM], bf[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(A + (wm * (BM / 2) + 16 * i + c) * TF::ARS + (kk * 32 + 8 * g) * 2);
+        for (int i = 0; i < TM; ++i) {
+          const int r = wm * (BM / 2) + 16 * i + c;
+          af[i] = *reinterpret_cast<const bf16x8*>(A + r * TF::ARS + TF::pos(r, 4 * kk + g) * 16);
+        }
 #pragma unroll
-        for (int t = 0; t < TN; ++t)
-          bf[t] = *reinterpret_cast<const bf16x8*>(B + (wn * (BN / 2) + 16 * t + c) * TF::BRS + (kk * 32 + 8 * g) * 2);
+        for (int t = 0; t < TN; ++t) {
+          const int r = wn * (BN / 2) + 16 * t + c;
+          bf[t] = *reinterpret_cast<const bf16x8*>(B + r * TF::BRS + TF::pos(r, 4 * kk + g) * 16);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -237,7 +274,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
   // in flight.  STG is even, so the LDS buffer index kt % 2 = st % 2 is a
   // compile-time constant.
   static_assert(STG % 2 == 0, "even number of load stages");
-  const int KTP = (KT + STG - 1) / STG * STG;
+  const int KTP = (KTg + STG - 1) / STG * STG;
 
   // prologue: steps 0 .. STG-1 in flight, step 0 decoded into LDS buffer 0,
   // then its register stage refilled with step STG
@@ -260,6 +297,30 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
       gload(kt + 1 + STG, xa[nx], wb[nx], sb[nx]);
       __syncthreads();
     }
+  }
+
+  // ---- sum the K groups: groups 1.. store their tiles into the (now idle)
+  // tile buffers, group 0 adds them in group order
+  if constexpr (KS > 1) {
+    float* red = reinterpret_cast<float*>(smem);
+    if (kg > 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          *reinterpret_cast<f32x4*>(red + ((((kg - 1) * 4 + wave) * TM * TN + i * TN + t) * 64 + lane) * 4) = acc[i][t];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g2 = 1; g2 < KS; ++g2)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((((g2 - 1) * 4 + wave) * TM * TN + i * TN + t) * 64 + lane) * 4);
+          acc[i][t] += o;
+        }
   }
 
   // ---- epilogue: lane holds D[4g + r][c] of every 16x16 tile; the column
@@ -286,24 +347,29 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(LinearArgs a) {
   }
 }
 
-template <int F, int BM, int BN>
+template <int F, int BM, int BN, int KS>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
-  constexpr int sm = tile_smem<F, BM, BN>();
+  constexpr int sm = KS * tile_smem<F, BM, BN>();
+  static_assert(sm <= 160 * 1024, "tile exceeds the LDS of a CU");
+  static_assert(KS == 1 || (KS - 1) * BM * BN * 4 <= sm, "group partials must fit in the tile buffers");
   static std::atomic<int> done{0};
-  auto k = k_gemm_tiled<F, BM, BN, tile_stages<BM, BN>()>;
+  auto k = k_gemm_tiled<F, BM, BN, tile_stages<BM, BN>(), KS>;
   hipError_t e = allow_smem(k, sm, done);
   if (e != hipSuccess) return e;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
-  k<<<grid, 256, sm, s>>>(a);
+  k<<<grid, 256 * KS, sm, s>>>(a);
   return hipGetLastError();
 }
 
 template <int F>
 hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  if (p.bm == 128 && p.bn == 128) return launch_tile<F, 128, 128>(a, s);
-  if (p.bm == 128) return launch_tile<F, 128, 64>(a, s);
-  if (p.bn == 128) return launch_tile<F, 64, 128>(a, s);
-  return launch_tile<F, 64, 64>(a, s);
+  // LDS bounds the K groups: 128 x 128 tiles run alone, 128 x 64 and 64 x 128
+  // with up to 2 groups, 64 x 64 with up to 4
+  if (p.bm == 128 && p.bn == 128) return launch_tile<F, 128, 128, 1>(a, s);
+  if (p.bm == 128) return p.ks >= 2 ? launch_tile<F, 128, 64, 2>(a, s) : launch_tile<F, 128, 64, 1>(a, s);
+  if (p.bn == 128) return p.ks >= 2 ? launch_tile<F, 64, 128, 2>(a, s) : launch_tile<F, 64, 128, 1>(a, s);
+  if (p.ks >= 4) return launch_tile<F, 64, 64, 4>(a, s);
+  return p.ks == 2 ? launch_tile<F, 64, 64, 2>(a, s) : launch_tile<F, 64, 64, 1>(a, s);
 }
 
 }  // namespace

@@ -52,17 +52,30 @@ namespace {
 // (g, c) to hold row c, K-chunk g, so loading it straight from a row-major X
 // touches 16 rows per load instruction.  With XLDS each wave instead loads
 // its [16*MT rows x one K macro-step] slice with contiguous 16-byte loads
-// (L lanes per row, R rows per instruction), writes it into a private padded
-// LDS slot and reads it back in the operand layout.
+// (L lanes per row, R rows per instruction), writes it into a private LDS slot
+// and reads it back in the operand layout.
+//
+// Slot layout: row r holds its L 16-byte chunks in the order pos(r, k) -- an
+// XOR of the chunk index with a few row bits, chosen so that the operand
+// reads (each quarter-wave reads 16 different rows) and the contiguous writes
+// are free of LDS bank conflicts on gfx950 (checked with the
+// SQ_LDS_BANK_CONFLICT counter: an unswizzled or padded row costs the reads
+// twice the LDS cycles).
 template <int F, int MT>
 struct XStage {
   static constexpr int KPL = FmtT<F>::KPL;
   static constexpr int MACRO = 4 * KPL;
   static constexpr int XB = (F == KF_FP8S) ? 1 : 2;  // bytes per activation element
-  static constexpr int ROWB = MACRO * XB + 16;        // padded LDS row
+  static constexpr int ROWB = MACRO * XB;             // LDS row (no padding)
   static constexpr int SLOT = 16 * MT * ROWB;         // one wave's slice
-  static constexpr int L = MACRO * XB / 16;           // lanes per row
+  static constexpr int L = MACRO * XB / 16;           // lanes per row = chunks per row
   static constexpr int R = 64 / L;                    // rows per load instruction
+  static_assert(L == 4 || L == 8 || L == 16, "slot rows of 4, 8 or 16 chunks");
+  __device__ static __forceinline__ int pos(int r, int k) {
+    if constexpr (L == 16) return k ^ ((r & 3) | (((r >> 3) & 1) << 3));
+    else if constexpr (L == 8) return k ^ (((r >> 1) & 1) | (((r >> 3) & 1) << 2));
+    else return k ^ ((r >> 1) & 3);
+  }
 };
 
 // LDS: [activation slots of the NW waves (XLDS)][NW wave partials, fp32]
@@ -178,14 +191,15 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
         for (int i = 0; i < MT; ++i)
 #pragma unroll
           for (int j = 0; j < XL; ++j) {
-            const int q = i * XL + j;
-            *reinterpret_cast<u32x4*>(slot + (q * XS::R + lane / XS::L) * XS::ROWB + (lane % XS::L) * 16) = xv[st][i][j];
+            const int row = (i * XL + j) * XS::R + lane / XS::L;
+            *reinterpret_cast<u32x4*>(slot + row * XS::ROWB + XS::pos(row, lane % XS::L) * 16) = xv[st][i][j];
           }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
           for (int j = 0; j < XL; ++j)
-            xv[st][i][j] = *reinterpret_cast<const u32x4*>(slot + (16 * i + c) * XS::ROWB + (g * KPL + 8 * j) * XS::XB);
+            xv[st][i][j] = *reinterpret_cast<const u32x4*>(
+                slot + (16 * i + c) * XS::ROWB + XS::pos(16 * i + c, (g * KPL + 8 * j) * XS::XB / 16) * 16);
       }
       if constexpr (F == KF_INT4) {
         f32x4 tmp[MT][NTW], rs[MT];
@@ -428,6 +442,19 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
         p.bn = cb[1];
         break;
       }
+    }
+    // few tiles: split K over 2 or 4 groups of waves inside each workgroup so
+    // that every CU runs 8-16 waves (the K steps are latency-bound otherwise)
+    const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+    const int64_t steps = (K + 63) / 64;
+    p.ks = 1;
+    if (!(p.bm == 128 && p.bn == 128)) {
+#ifdef VAR_KS
+      p.ks = VAR_KS;
+#else
+      if (tiles <= 256 && steps >= 32 && p.bm == 64 && p.bn == 64) p.ks = 4;
+      else if (tiles <= 512 && steps >= 16) p.ks = 2;
+#endif
     }
     p.part_bytes = 0;
     p.ws_bytes = 0;
