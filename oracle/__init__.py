@@ -19,6 +19,8 @@ What it implements, and from which passage (the pages are the Torch-TensorRT
   error and the page's ``sqnr`` helper.
 * ``static_fp8`` -- calibration (absmax observers), activation Q and the
   static-FP8 Linear / two-layer model.
+* ``mx_dynamic`` -- dynamic MX quantization of activations and the MXFP4 x
+  MXFP4 Linear of the MXFP4 page's "Dynamic Activation + MX Weight" config.
 
 Arithmetic rules used throughout: bf16 inputs widen exactly to fp32; every
 quantizer step is an IEEE fp32 operation (numpy float32, correctly rounded);

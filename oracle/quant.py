@@ -179,6 +179,16 @@ def quantize_mxfp4(W_bf16, block=MXFP4_BLOCK):
     N, K = w.shape
     if N % block or K % block:
         raise ValueError("MXFP4 needs N and K divisible by 32")
+    return mx_blocks(w, block)
+
+
+def mx_blocks(w, block=MXFP4_BLOCK):
+    """The MX quantization steps of ``quantize_mxfp4`` on an fp32 matrix whose
+    rows are split into blocks of 32 consecutive elements (K % 32 == 0).
+    Returns (codes uint8 [R, K], scales uint8 E8M0 [R, K/32])."""
+    N, K = w.shape
+    if K % block:
+        raise ValueError("MX blocks need K divisible by 32")
     wb = w.reshape(N, K // block, block)
     ab = np.abs(wb).max(axis=2)
     _, ex = np.frexp(np.where(ab > 0, ab, F32(1.0)))

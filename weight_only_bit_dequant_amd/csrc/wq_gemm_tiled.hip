@@ -363,13 +363,12 @@ hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
 
 template <int F>
 hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  // LDS bounds the K groups: 128 x 128 tiles run alone, 128 x 64 and 64 x 128
-  // with up to 2 groups, 64 x 64 with up to 4
+  // 128 x 128 tiles are planned only when there are enough of them (no K
+  // groups); the other shapes run with one or two K groups
   if (p.bm == 128 && p.bn == 128) return launch_tile<F, 128, 128, 1>(a, s);
   if (p.bm == 128) return p.ks >= 2 ? launch_tile<F, 128, 64, 2>(a, s) : launch_tile<F, 128, 64, 1>(a, s);
   if (p.bn == 128) return p.ks >= 2 ? launch_tile<F, 64, 128, 2>(a, s) : launch_tile<F, 64, 128, 1>(a, s);
-  if (p.ks >= 4) return launch_tile<F, 64, 64, 4>(a, s);
-  return p.ks == 2 ? launch_tile<F, 64, 64, 2>(a, s) : launch_tile<F, 64, 64, 1>(a, s);
+  return p.ks >= 2 ? launch_tile<F, 64, 64, 2>(a, s) : launch_tile<F, 64, 64, 1>(a, s);
 }
 
 }  // namespace

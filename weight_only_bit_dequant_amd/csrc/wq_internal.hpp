@@ -36,7 +36,7 @@ struct LinearPlan {
   int gx, gz;     // workgroups along N and along M
   int S;          // K splits across workgroups
   int bm, bn;     // output tile of the tiled configuration
-  int ks;         // K groups inside a tiled workgroup (1, 2 or 4)
+  int ks;         // K groups inside a tiled workgroup (1 or 2)
   size_t part_bytes, ws_bytes;  // split-K partials (0 without a split)
 };
 

@@ -443,19 +443,14 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
         break;
       }
     }
-    // few tiles: split K over 2 or 4 groups of waves inside each workgroup so
-    // that every CU runs 8-16 waves (the K steps are latency-bound otherwise)
+    // few tiles: split K over two groups of waves inside each workgroup, so
+    // that each CU runs 8 waves (the K steps are latency-bound otherwise).
+    // Measured at M = 128 and 256 (N = 4096, K = 3072): two groups beat one by
+    // 10-25 %; four groups (64 x 64 tiles only) were slower than two.
     const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
     const int64_t steps = (K + 63) / 64;
     p.ks = 1;
-    if (!(p.bm == 128 && p.bn == 128)) {
-#ifdef VAR_KS
-      p.ks = VAR_KS;
-#else
-      if (tiles <= 256 && steps >= 32 && p.bm == 64 && p.bn == 64) p.ks = 4;
-      else if (tiles <= 512 && steps >= 16) p.ks = 2;
-#endif
-    }
+    if (!(p.bm == 128 && p.bn == 128) && tiles <= 512 && steps >= 16) p.ks = 2;
     p.part_bytes = 0;
     p.ws_bytes = 0;
     return p;
