@@ -195,23 +195,27 @@ def cpu_baseline(seconds_per_format=3.0):
 
 def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
     """The other workload points, reported beside the M=32 line: MXFP4 at
-    M in {1, 32, 256, 4096} and the static-FP8 layer at M=4096, each timed as a
-    graph of back-to-back launches over the same cold weight copies.  Large M
-    is bound by the matrix cores: FLOP/s against the dense bf16 (MXFP4) or FP8
-    (static) peak."""
+    M in {1, 32, 256, 4096}, the static-FP8 layer at M=4096 and the MXFP4
+    dynamic-activation path (MX act Q + E2M1 x E2M1 GEMM) at M in {32, 256,
+    4096}, each timed as a graph of back-to-back launches over the same cold
+    weight copies.  Large M is bound by the matrix cores: FLOP/s against the
+    dense bf16 (MXFP4 weight-only), FP8 (static) or FP4 (MX dynamic) peak."""
     import torch
 
     from weight_only_bit_dequant_amd import synth, wq
 
     res = {}
-    peak = {"mxfp4": 2500.0, "static_fp8": 5000.0}  # dense TFLOP/s (bf16 / fp8)
-    for fmt, Ms in (("mxfp4", (1, 32, 256, 4096)), ("static_fp8", (32, 4096))):
-        lay = layers[fmt]
+    peak = {"mxfp4": 2500.0, "static_fp8": 5000.0, "mxfp4_dynamic": 10100.0}  # dense TFLOP/s (bf16 / fp8 / fp4)
+    for fmt, Ms in (("mxfp4", (1, 32, 256, 4096)), ("static_fp8", (32, 4096)), ("mxfp4_dynamic", (32, 256, 4096))):
+        lay = layers["mxfp4" if fmt == "mxfp4_dynamic" else fmt]  # the same cold weight copies
         for Mv in Ms:
-            X = synth.as_torch_bf16(synth.activations(Mv, K, synth.SEED_X + synth.WORKLOADS[fmt]["cfg"]), dev)
+            base = "mxfp4" if fmt == "mxfp4_dynamic" else fmt
+            X = synth.as_torch_bf16(synth.activations(Mv, K, synth.SEED_X + synth.WORKLOADS[base]["cfg"]), dev)
             Y = torch.empty((Mv, N), dtype=torch.bfloat16, device=dev)
             if fmt == "static_fp8":
                 ws = torch.zeros(max(1, wq.wq_fp8_static_workspace(Mv, N, K)), dtype=torch.uint8, device=dev)
+            elif fmt == "mxfp4_dynamic":
+                ws = torch.zeros(max(1, wq.wq_mxfp4_dynamic_workspace(Mv, K)), dtype=torch.uint8, device=dev)
             else:
                 ws = torch.zeros(max(1, wq.wq_linear_workspace("mxfp4", Mv, N, K)), dtype=torch.uint8, device=dev)
 
@@ -220,6 +224,8 @@ def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
                     r = lay["reps"][i % len(lay["reps"])]
                     if fmt == "static_fp8":
                         wq.wq_fp8_static_linear(X, lay["act_scale"], r["packed"], r["scales"], None, Y, ws)
+                    elif fmt == "mxfp4_dynamic":
+                        wq.wq_mxfp4_dynamic_linear(X, r["packed"], r["scales"], lay["bias"], N, Y, ws)
                     else:
                         wq.wq_linear("mxfp4", X, r["packed"], r["scales"], None, lay["bias"], N, Y, ws)
 
@@ -234,13 +240,13 @@ def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
             torch.cuda.synchronize()
             us = a.elapsed_time(b) * 1e3 / reps
             flop = 2.0 * Mv * N * K
-            eff = effective_bytes(fmt)
+            eff = effective_bytes(base)
             res[f"{fmt}_M{Mv}"] = {
                 "us_per_launch": round(us, 3),
                 "TFLOPs": round(flop / (us * 1e-6) / 1e12, 2),
                 "pct_mfma_peak": round(100.0 * flop / (us * 1e-6) / 1e12 / peak[fmt], 2),
                 "effective_TBps": round(eff / (us * 1e-6) / 1e12, 4),
-                "launches": 2 if fmt == "static_fp8" else 1,
+                "launches": 1 if fmt == "mxfp4" else 2,
             }
             del g
     return res

@@ -213,6 +213,33 @@ wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_s
                         size_t workspace_bytes, void* stream);
 
 /*
+ * MXFP4 dynamic-activation x MXFP4-weight Linear ("TorchAO MXFP4 Dynamic
+ * Activation + MX Weight (Linear)", intro: weights MXFP4, activations
+ * quantized to MX on every call, the GEMM on native MXFP4 matrix units).
+ *
+ * wq_mx_quantize_act: X bf16 [M][K] -> Xq packed E2M1 [M][K/2] (element 2j in
+ * the low nibble of byte j) and Xs E8M0 [M][K/32], with the MXFP4 weight rule
+ * applied to each 32-element block of a row (e = floor(log2 max|x|) - 2,
+ * clamped to [-127, 127]; codes E2M1(clamp(x / 2^e, +-6)), nearest even, sign
+ * kept).  K % 32 == 0; any M.
+ *
+ * wq_mx_linear: Y = bf16(sum_k deq(Xq)[m][k] deq(Wq)[n][k] (+ bias[n])) on the
+ * E2M1 x E2M1 scaled matrix cores (fp32 accumulation).  Wq/Ws: the packed
+ * weight and E8M0 scales of wq_quantize + wq_pack for WQ_MXFP4.  N % 32 == 0,
+ * K % 32 == 0.  No workspace.
+ *
+ * wq_mxfp4_dynamic_linear: wq_mx_quantize_act into the workspace, then
+ * wq_mx_linear.  Workspace: wq_mxfp4_dynamic_workspace(M, K) bytes.
+ */
+wq_status wq_mx_quantize_act(const void* X, int64_t M, int64_t K, void* Xq, void* Xs, void* stream);
+wq_status wq_mx_linear(const void* Xq, const void* Xs, int64_t M, int64_t K, const void* Wq, const void* Ws,
+                       const void* bias, int64_t N, void* Y, void* stream);
+size_t wq_mxfp4_dynamic_workspace(int64_t M, int64_t K);
+wq_status wq_mxfp4_dynamic_linear(const void* X, int64_t M, int64_t K, const void* Wq, const void* Ws,
+                                  const void* bias, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * Measurement aid (not part of the method): reads `bytes` bytes at `p` with
  * 16-byte vector loads, as the plain read-only stream that a weight stream of
  * the same size is compared against.  sink[b] (device, wq_read_stream_words

@@ -113,6 +113,20 @@ def test_quantize_pack_dequant_validation():
     assert L.wq_fp8_linear(v(16), 0, 32, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.OK
     assert L.wq_fp8_linear(v(16), 32, 3072, v(16), v(16), v(16), None, 256, v(16), None, 0,
                            None) == wq.EWORKSPACE  # narrow layer: split K
+    # MXFP4 dynamic-activation path
+    assert L.wq_mx_quantize_act(v(16), 4, 48, v(16), v(16), None) == wq.ESHAPE
+    assert L.wq_mx_quantize_act(v(16), 4, 64, None, v(16), None) == wq.EINVAL
+    assert L.wq_mx_quantize_act(v(8), 4, 64, v(16), v(16), None) == wq.EALIGN
+    assert L.wq_mx_quantize_act(None, 0, 64, None, None, None) == wq.OK
+    assert L.wq_mx_linear(v(16), v(16), 4, 64, v(16), v(16), None, 48, v(16), None) == wq.ESHAPE  # N % 32
+    assert L.wq_mx_linear(v(16), v(16), 4, 48, v(16), v(16), None, 64, v(16), None) == wq.ESHAPE  # K % 32
+    assert L.wq_mx_linear(v(16), None, 4, 64, v(16), v(16), None, 64, v(16), None) == wq.EINVAL
+    assert L.wq_mx_linear(v(16), v(16), 4, 64, v(16), v(16), None, 64, v(24), None) == wq.EALIGN
+    need = wq.wq_mxfp4_dynamic_workspace(32, 3072)
+    assert need >= 32 * 1536 + 32 * 96
+    assert L.wq_mxfp4_dynamic_linear(v(16), 32, 3072, v(16), v(16), None, 4096, v(16), v(16), need - 1,
+                                     None) == wq.EWORKSPACE
+    assert L.wq_mxfp4_dynamic_linear(v(16), 0, 3072, v(16), v(16), None, 4096, v(16), None, 0, None) == wq.OK
     # read-only stream (measurement aid)
     assert L.wq_read_stream(v(16), 0, None, None) == wq.OK
     assert L.wq_read_stream(None, 64, v(16), None) == wq.EINVAL

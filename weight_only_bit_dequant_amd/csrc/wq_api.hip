@@ -296,6 +296,75 @@ wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_s
                        workspace_bytes, stream);
 }
 
+wq_status wq_mx_quantize_act(const void* X, int64_t M, int64_t K, void* Xq, void* Xs, void* stream) {
+  if (M < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
+  if (K % 32) return fail(WQ_ESHAPE, "MX activation blocks need K %% 32 == 0 (K=%lld)", (long long)K);
+  if (M > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (M == 0 || K == 0) return ok();
+  if (2 * M * K >= kMaxBufferBytes) return fail(WQ_EUNSUPPORTED, "activation buffer of 2^31 bytes or more");
+  if (!X || !Xq || !Xs) return fail(WQ_EINVAL, "wq_mx_quantize_act: null pointer");
+  if (!aligned16(X) || !aligned16(Xq)) return fail(WQ_EALIGN, "X and Xq must be 16-byte aligned");
+  return hip_status(wq::launch_mx_quantize_act((const uint16_t*)X, M, K, (uint8_t*)Xq, (uint8_t*)Xs,
+                                               (hipStream_t)stream),
+                    "wq_mx_quantize_act launch");
+}
+
+wq_status wq_mx_linear(const void* Xq, const void* Xs, int64_t M, int64_t K, const void* Wq, const void* Ws,
+                       const void* bias, int64_t N, void* Y, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
+  wq_status st = check_shape_rule(WQ_MXFP4, N, K);
+  if (st != WQ_OK) return st;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (M == 0 || N == 0) return ok();
+  if (K == 0) return fail(WQ_EUNSUPPORTED, "K == 0");
+  if (N * K / 2 >= kMaxBufferBytes || M * K / 2 >= kMaxBufferBytes)
+    return fail(WQ_EUNSUPPORTED, "weight or activation buffer of 2^31 bytes or more");
+  if (K >= ((int64_t)1 << 22)) return fail(WQ_EUNSUPPORTED, "K of 2^22 or more");
+  if (!Xq || !Xs || !Wq || !Ws || !Y) return fail(WQ_EINVAL, "wq_mx_linear: null pointer");
+  if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(Y)) return fail(WQ_EALIGN, "Xq, Wq and Y must be 16-byte aligned");
+  wq::LinearArgs a{};
+  a.X = Xq;
+  a.xscales = (const uint8_t*)Xs;
+  a.W = Wq;
+  a.scales = Ws;
+  a.bias = (const uint16_t*)bias;
+  a.Y = (uint16_t*)Y;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  return hip_status(wq::launch_mx_linear(a, (hipStream_t)stream), "wq_mx_linear launch");
+}
+
+size_t wq_mxfp4_dynamic_workspace(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return align256((size_t)M * (size_t)K / 2) + align256((size_t)M * (size_t)(K / 32));
+}
+
+wq_status wq_mxfp4_dynamic_linear(const void* X, int64_t M, int64_t K, const void* Wq, const void* Ws,
+                                  const void* bias, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
+  wq_status st = check_shape_rule(WQ_MXFP4, N, K);
+  if (st != WQ_OK) return st;
+  if (M == 0 || N == 0) return ok();
+  const size_t need = wq_mxfp4_dynamic_workspace(M, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(WQ_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(WQ_EALIGN, "workspace must be 16-byte aligned");
+  if (!X || !Wq || !Ws || !Y) return fail(WQ_EINVAL, "wq_mxfp4_dynamic_linear: null pointer");
+  // validate the GEMM before anything is enqueued
+  void* xq = workspace;
+  void* xs = (char*)workspace + align256((size_t)M * (size_t)K / 2);
+  if (K == 0) return fail(WQ_EUNSUPPORTED, "K == 0");
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(Y)) return fail(WQ_EALIGN, "X, Wq and Y must be 16-byte aligned");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (N * K / 2 >= kMaxBufferBytes || 2 * M * K >= kMaxBufferBytes || K >= ((int64_t)1 << 22))
+    return fail(WQ_EUNSUPPORTED, "buffer of 2^31 bytes or more, or K of 2^22 or more");
+  st = wq_mx_quantize_act(X, M, K, xq, xs, stream);
+  if (st != WQ_OK) return st;
+  return wq_mx_linear(xq, xs, M, K, Wq, Ws, bias, N, Y, stream);
+}
+
 size_t wq_read_stream_words(size_t bytes) { return (bytes + 16383) / 16384; }
 
 wq_status wq_read_stream(const void* p, size_t bytes, uint32_t* sink, void* stream) {

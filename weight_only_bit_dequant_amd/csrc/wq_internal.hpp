@@ -48,6 +48,7 @@ struct LinearArgs {
   const void* scales;    // format scales
   const float* gscale;   // NVFP4 global scale (device)
   const float* act_scale;  // static FP8 activation scale (device)
+  const uint8_t* xscales;  // E8M0 activation block scales [M][K/32] (MX path)
   const uint16_t* bias;  // bf16 [N] or null
   uint16_t* Y;           // bf16 [M][N]
   float* part;           // split-K partials (workspace)
@@ -67,5 +68,8 @@ hipError_t launch_absmax(const uint16_t* X, int64_t numel, float* amax, hipStrea
 hipError_t launch_fp8_scale(const float* amax, float* scale, int64_t count, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* X, int64_t numel, const float* act_scale, uint8_t* Xq,
                                hipStream_t s);
+// MXFP4 dynamic-activation path
+hipError_t launch_mx_quantize_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, uint8_t* Xs, hipStream_t s);
+hipError_t launch_mx_linear(const LinearArgs& a, hipStream_t s);
 
 }  // namespace wq

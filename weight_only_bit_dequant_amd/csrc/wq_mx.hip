@@ -1,0 +1,386 @@
+// MXFP4 dynamic-activation x MXFP4-weight Linear on the gfx950 scaled matrix
+// cores.
+//
+// "TorchAO MXFP4 Dynamic Activation + MX Weight (Linear)", intro: the weights
+// are MXFP4 (E2M1 codes, E8M0 scale per 32 K); the activations are quantized
+// to MX on every call, and on hardware with MXFP4 matrix units the GEMM
+// multiplies the two MX operands directly.  Here the activations get the same
+// MXFP4 rule as the weights, and v_mfma_scale_f32_16x16x128_f8f6f4 takes both
+// E2M1 operands and their E8M0 block scales as they are stored: no decode.
+//
+// Operand layout (checked on the device against a host model): in one
+// 16x16x128 MFMA, lane (g, c) supplies 16 bytes = 32 E2M1 codes of row c (A)
+// or column c (B), K 32g .. 32g+31 of the step, low nibble first, plus the
+// E8M0 scale of exactly that 32-element block; the result D[4g + r][c] lands
+// in element r of lane (g, c).  A packed row of K/2 bytes and its [K/32]
+// scale row therefore feed the MFMA with one 16-byte and one 1-byte load per
+// lane and step.
+#include "wq_kernel_common.hpp"
+
+namespace wq {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+__device__ __forceinline__ f32x4 mfma_mx4(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb, f32x4 c) {
+  const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  // cbsz = blgp = 4: both operands E2M1; byte 0 of each scale register
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// ---------------------------------------------------------------- activation quantizer
+// One thread per 32-element block of a row: the block's max |x| sets
+// e = floor(log2 amax) - 2 (from the bf16 exponent field; zero and subnormal
+// maxima give the clamp value -127), scale code e + 127, and the codes are
+// E2M1(x * 2^-e) -- an exact power-of-two product -- converted with
+// v_cvt_scalef32_pk_fp4_f32 (nearest even, saturating at 6, sign kept:
+// checked against the reference encoder on the device).  The 32 codes are
+// stored packed (element 2j in the low nibble of byte j).
+__global__ __launch_bounds__(256) void k_mx_quant_act(const uint16_t* __restrict__ X, uint32_t nblk,
+                                                      uint8_t* __restrict__ Xq, uint8_t* __restrict__ Xs) {
+  const uint32_t blk = blockIdx.x * 256u + threadIdx.x;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(X, nblk * 64u);
+  u32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = bload128(r, blk * 64u + 16u * q);
+  uint32_t amax = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = v[q][w] & 0x7FFFu, hi = (v[q][w] >> 16) & 0x7FFFu;
+      amax = max(amax, max(lo, hi));
+    }
+  const int E = (int)(amax >> 7);
+  const int e = max(E - 129, -127);  // zero, subnormal and [2^-126, 2^-125) maxima clamp to -127
+  const float inv = bitsf((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 125]
+  // bf16 pair word -> two scaled fp32 values (element 2j in the low half)
+#define WQ_LO(u) (bitsf((u) << 16) * inv)
+#define WQ_HI(u) (bitsf((u) & 0xFFFF0000u) * inv)
+  u32x4 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t word = 0;
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, WQ_LO(v[q].x), WQ_HI(v[q].x), 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, WQ_LO(v[q].y), WQ_HI(v[q].y), 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, WQ_LO(v[q].z), WQ_HI(v[q].z), 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, WQ_LO(v[q].w), WQ_HI(v[q].w), 1.0f, 3);
+    out[q] = word;
+  }
+#undef WQ_LO
+#undef WQ_HI
+  if (blk < nblk) {
+    *reinterpret_cast<u32x4*>(Xq + (size_t)blk * 16) = out;
+    Xs[blk] = (uint8_t)(e + 127);
+  }
+}
+
+// ---------------------------------------------------------------- small-M GEMM
+// One workgroup = 12 waves = 16 output columns x 16*MT rows x all of K; wave w
+// owns 128-K steps w*SPW .. w*SPW+SPW-1 (+ 12*SPW per pass).  Every load of a
+// pass (packed weight, weight scales, packed activations, activation scales)
+// is issued before the first MFMA; out-of-range offsets read zero codes and
+// zero scale bytes, whose products are zero.  Wave partials are reduced
+// through LDS as in the bf16 kernel.
+template <int MT>
+__global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
+  constexpr int NW = 12, SPW = 2, NT = 16, NTHR = NW * 64;
+  constexpr int E = MT * 16 * NT;
+  __shared__ __attribute__((aligned(16))) float red[NW * E];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int n0 = blockIdx.x * NT, m0 = blockIdx.z * (16 * MT);
+  const int M = a.M, N = a.N, K = a.K;
+  const int T = (K + 127) / 128;
+  const uint32_t rowb = (uint32_t)K / 2u, srow = (uint32_t)K / 32u;
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * rowb);
+  const __amdgpu_buffer_rsrc_t Wsr = make_rsrc(a.scales, (uint32_t)N * srow);
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * rowb);
+  const __amdgpu_buffer_rsrc_t Xsr = make_rsrc(a.xscales, (uint32_t)M * srow);
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  const int ecol = tid % NT, en = n0 + ecol;
+  const uint32_t bias_bits = bload16(Br, (uint32_t)en * 2u);
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = wave * SPW; s0 < T; s0 += NW * SPW) {
+    u32x4 w[SPW], x[SPW][MT];
+    uint32_t ws[SPW], xs[SPW][MT];
+#pragma unroll
+    for (int st = 0; st < SPW; ++st) {
+      const int k = (s0 + st) * 128 + 32 * g;  // first K of this lane's block
+      const bool kv = k < K;
+      const uint32_t n = (uint32_t)(n0 + c);
+      w[st] = bload128(Wr, off_if(kv, n * rowb + (uint32_t)k / 2u));
+      ws[st] = bload8(Wsr, off_if(kv, n * srow + (uint32_t)k / 32u));
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const uint32_t m = (uint32_t)(m0 + 16 * i + c);
+        x[st][i] = bload128(Xr, off_if(kv, m * rowb + (uint32_t)k / 2u));
+        xs[st][i] = bload8(Xsr, off_if(kv, m * srow + (uint32_t)k / 32u));
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < SPW; ++st)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[i] = mfma_mx4(x[st][i], xs[st][i], w[st], ws[st], acc[i]);
+  }
+
+  // wave partials -> LDS, one barrier, per-thread sums in wave order
+#pragma unroll
+  for (int i = 0; i < MT; ++i) *reinterpret_cast<f32x4*>(red + ((wave * MT + i) * 64 + lane) * 4) = acc[i];
+  __syncthreads();
+  if (tid < E) {
+    const int row = tid / NT, col = tid % NT;
+    const int idx = ((row >> 4) * 64 + 16 * ((row >> 2) & 3) + col) * 4 + (row & 3);
+    float v = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) v += red[w2 * E + idx];
+    const int m = m0 + row;
+    if (m < M && en < N) a.Y[(int64_t)m * N + en] = f32_to_bf16(v + bitsf(bias_bits << 16));
+  }
+}
+
+// ---------------------------------------------------------------- tiled GEMM (larger M)
+// One workgroup (4 waves, 2 x 2) computes a BM x BN tile; K advances 128 per
+// step (one scaled MFMA deep).  Per step every thread loads its share of the
+// packed activation and weight tiles (16-byte chunks, 64 bytes per row) one
+// step ahead and stores them to a double-buffered LDS tile as they are:
+// nothing is decoded.  Each wave then reads 16-byte operand chunks and scale
+// bytes from LDS and issues (BM/32) x (BN/32) MFMAs.  LDS rows hold their four
+// 16-byte chunks XOR-swizzled with row bits 1-2, which keeps both the operand
+// reads and the row writes free of bank conflicts.
+//
+// Scales: with PRE, the workgroup copies its BM activation and BN weight
+// scale rows (K/32 bytes each, contiguous in memory) into LDS once, with
+// 16-byte loads, before the K loop.  Without PRE (scale rows not 16-byte
+// multiples, or too long for LDS) every step loads 4 scale bytes per row;
+// those loads touch a different row per lane and were measured to dominate
+// the step time when they are used.
+template <int BM, int BN>
+struct MxTile {
+  static constexpr int ROWB = 64;                       // packed bytes of one row per step
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  static constexpr int AS_BYTES = BM * 4, BS_BYTES = BN * 4;  // per-step scale planes (no PRE)
+  static constexpr int BUF = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
+  static constexpr int TILES = 2 * BUF;
+  static constexpr int NA = BM * 4 / 256, NB = BN * 4 / 256;  // 16-byte chunks per thread
+  __device__ static __forceinline__ int pos(int r, int k) { return k ^ ((r >> 1) & 3); }
+  // LDS for the whole-K scale rows (PRE)
+  static size_t pre_bytes(int K) { return (size_t)(BM + BN) * (size_t)(K / 32); }
+};
+
+template <int BM, int BN, bool PRE>
+__global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
+  using TT = MxTile<BM, BN>;
+  constexpr int TM = BM / 32, TN = BN / 32;
+  static_assert(TT::NA >= 1 && TT::NB >= 1, "tile rows must cover the 256 threads");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int M = a.M, N = a.N, K = a.K;
+
+  // XCD-aware tile order (see the bf16 tiled kernel)
+  const int gx = gridDim.x, G = gx * gridDim.y;
+  int b = blockIdx.y * gx + blockIdx.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int n0 = (b % gx) * BN, m0 = (b / gx) * BM;
+
+  const uint32_t rowb = (uint32_t)K / 2u, srow = (uint32_t)K / 32u;
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * rowb);
+  const __amdgpu_buffer_rsrc_t Xsr = make_rsrc(a.xscales, (uint32_t)M * srow);
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * rowb);
+  const __amdgpu_buffer_rsrc_t Wsr = make_rsrc(a.scales, (uint32_t)N * srow);
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  const int KT = (K + 127) / 128;
+  unsigned char* XS = smem + TT::TILES;    // PRE: [BM][srow] activation scale rows
+  unsigned char* WS = XS + BM * srow;      //      [BN][srow] weight scale rows
+
+  if constexpr (PRE) {
+    // rows m0 .. m0+BM-1 of the scale matrix are one contiguous byte range;
+    // 16-byte chunks, rows past M / N read zero
+    const int xchunks = BM * (int)srow / 16, wchunks = BN * (int)srow / 16;
+    for (int q = tid; q < xchunks; q += 256)
+      *reinterpret_cast<u32x4*>(XS + 16 * q) = bload128(Xsr, (uint32_t)m0 * srow + 16u * q);
+    for (int q = tid; q < wchunks; q += 256)
+      *reinterpret_cast<u32x4*>(WS + 16 * q) = bload128(Wsr, (uint32_t)n0 * srow + 16u * q);
+  }
+
+  // loads of one step: chunk q of this thread is row (q*256 + tid) / 4, part % 4
+  u32x4 xa[2][TT::NA], wb[2][TT::NB];
+  uint32_t xsb[2][4], wsb[2][4];  // raw scale bytes (no PRE)
+  auto gload = [&](int kt, int st) {
+    const uint32_t kb = (uint32_t)kt * 64u;  // byte offset of the step in a packed row
+#pragma unroll
+    for (int q = 0; q < TT::NA; ++q) {
+      const int id = q * 256 + tid, row = id >> 2, part = id & 3;
+      const bool ok = kt * 128 + part * 32 < K;
+      xa[st][q] = bload128(Xr, off_if(ok, (uint32_t)(m0 + row) * rowb + kb + 16u * part));
+    }
+#pragma unroll
+    for (int q = 0; q < TT::NB; ++q) {
+      const int id = q * 256 + tid, row = id >> 2, part = id & 3;
+      const bool ok = kt * 128 + part * 32 < K;
+      wb[st][q] = bload128(Wr, off_if(ok, (uint32_t)(n0 + row) * rowb + kb + 16u * part));
+    }
+    if constexpr (!PRE) {
+      // thread t reads the step's 4 scale bytes of activation row t % BM and
+      // weight row t % BN (threads past the row count repeat a row, so no
+      // thread needs a branch); bytes past K read zero
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool okj = kt * 128 + 32 * j < K;
+        xsb[st][j] = bload8(Xsr, off_if(okj, (uint32_t)(m0 + tid % BM) * srow + (uint32_t)kt * 4u + j));
+        wsb[st][j] = bload8(Wsr, off_if(okj, (uint32_t)(n0 + tid % BN) * srow + (uint32_t)kt * 4u + j));
+      }
+    }
+  };
+  auto lstore = [&](int buf, int st) {
+    unsigned char* A = smem + buf * TT::BUF;
+    unsigned char* B = A + TT::A_BYTES;
+#pragma unroll
+    for (int q = 0; q < TT::NA; ++q) {
+      const int id = q * 256 + tid, row = id >> 2, part = id & 3;
+      *reinterpret_cast<u32x4*>(A + row * TT::ROWB + TT::pos(row, part) * 16) = xa[st][q];
+    }
+#pragma unroll
+    for (int q = 0; q < TT::NB; ++q) {
+      const int id = q * 256 + tid, row = id >> 2, part = id & 3;
+      *reinterpret_cast<u32x4*>(B + row * TT::ROWB + TT::pos(row, part) * 16) = wb[st][q];
+    }
+    if constexpr (!PRE) {
+      // scale planes [block j][row]: byte stores straight from the loaded
+      // registers, BM apart, so the compiler does not merge them into words
+      // (which would make it wait for all four loads); repeated rows store
+      // identical bytes
+      unsigned char* AS = B + TT::B_BYTES;
+      unsigned char* BS = AS + TT::AS_BYTES;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        AS[j * BM + tid % BM] = (unsigned char)xsb[st][j];
+        BS[j * BN + tid % BN] = (unsigned char)wsb[st][j];
+      }
+    }
+  };
+
+  uint32_t bias_bits[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) bias_bits[t] = bload16(Br, (uint32_t)(n0 + wn * (BN / 2) + 16 * t + c) * 2u);
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf, int kt) {
+    const unsigned char* A = smem + buf * TT::BUF;
+    const unsigned char* B = A + TT::A_BYTES;
+    const unsigned char* AS = B + TT::B_BYTES;
+    const unsigned char* BS = AS + TT::AS_BYTES;
+    u32x4 af[TM], bf[TN];
+    uint32_t as[TM], bs[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * (BM / 2) + 16 * i + c;
+      af[i] = *reinterpret_cast<const u32x4*>(A + r * TT::ROWB + TT::pos(r, g) * 16);
+      // blocks past K have zero codes; their scale is taken as 2^0
+      as[i] = PRE ? ((4 * kt + g < (int)srow) ? XS[r * srow + min(4 * kt + g, (int)srow - 1)] : 127u) : AS[g * BM + r];
+    }
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int r = wn * (BN / 2) + 16 * t + c;
+      bf[t] = *reinterpret_cast<const u32x4*>(B + r * TT::ROWB + TT::pos(r, g) * 16);
+      bs[t] = PRE ? ((4 * kt + g < (int)srow) ? WS[r * srow + min(4 * kt + g, (int)srow - 1)] : 127u) : BS[g * BN + r];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int t = 0; t < TN; ++t) acc[i][t] = mfma_mx4(af[i], as[i], bf[t], bs[t], acc[i][t]);
+  };
+
+  // two register stages, two LDS buffers; the step count is even so both
+  // indices are compile-time constants in the unrolled pair (steps past K
+  // read zero codes)
+  const int KTP = (KT + 1) / 2 * 2;
+  gload(0, 0);
+  gload(1, 1);
+  lstore(0, 0);
+  gload(2, 0);
+  __syncthreads();
+  for (int kt = 0; kt < KTP; kt += 2) {
+    compute(0, kt);
+    lstore(1, 1);
+    gload(kt + 3, 1);
+    __syncthreads();
+    compute(1, kt + 1);
+    lstore(0, 0);
+    gload(kt + 4, 0);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int n = n0 + wn * (BN / 2) + 16 * t + c;
+    const float bias = bitsf(bias_bits[t] << 16);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
+        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][t][r] + bias);
+      }
+  }
+}
+
+template <int BM, int BN>
+hipError_t launch_mx_tile(const LinearArgs& a, hipStream_t s) {
+  using TT = MxTile<BM, BN>;
+  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+  const size_t pre = TT::pre_bytes(a.K);
+  if ((a.K / 32) % 16 == 0 && TT::TILES + pre <= 96 * 1024) {
+    static std::atomic<int> done{0};
+    const int sm = (int)(TT::TILES + pre);
+    auto k = k_mx_gemm_tiled<BM, BN, true>;
+    if (sm > 65536 && !done.load(std::memory_order_acquire)) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         96 * 1024);
+      if (e != hipSuccess) return e;
+      done.store(1, std::memory_order_release);
+    }
+    k<<<grid, 256, sm, s>>>(a);
+  } else {
+    k_mx_gemm_tiled<BM, BN, false><<<grid, 256, TT::TILES, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mx_quantize_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, uint8_t* Xs, hipStream_t s) {
+  const uint32_t nblk = (uint32_t)(M * (K / 32));
+  k_mx_quant_act<<<(nblk + 255) / 256, 256, 0, s>>>(X, nblk, Xq, Xs);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_linear(const LinearArgs& a, hipStream_t s) {
+  if (a.M > 64) {
+    // matrix-core bound: tiles of 128 x 128 when they fill the chip, else 64 x 64
+    const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+    return t128 >= 192 ? launch_mx_tile<128, 128>(a, s) : launch_mx_tile<64, 64>(a, s);
+  }
+  const int gx = (a.N + 15) / 16;
+  if (a.M <= 16) {
+    k_mx_linear<1><<<dim3(gx, 1, (a.M + 15) / 16), 768, 0, s>>>(a);
+  } else {
+    k_mx_linear<2><<<dim3(gx, 1, (a.M + 31) / 32), 768, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wq

@@ -64,12 +64,17 @@ def lib():
         L.wq_fp8_linear_workspace.argtypes = [I64, I64, I64]
         L.wq_fp8_linear_workspace.restype = SZ
         L.wq_fp8_linear.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, SZ, P]
+        L.wq_mx_quantize_act.argtypes = [P, I64, I64, P, P, P]
+        L.wq_mx_linear.argtypes = [P, P, I64, I64, P, P, P, I64, P, P]
+        L.wq_mxfp4_dynamic_workspace.argtypes = [I64, I64]
+        L.wq_mxfp4_dynamic_workspace.restype = SZ
+        L.wq_mxfp4_dynamic_linear.argtypes = [P, I64, I64, P, P, P, I64, P, P, SZ, P]
         L.wq_read_stream.argtypes = [P, SZ, P, P]
         L.wq_read_stream_words.argtypes = [SZ]
         L.wq_read_stream_words.restype = SZ
         for name in ("wq_layout", "wq_quantize", "wq_pack", "wq_dequantize", "wq_linear", "wq_absmax",
                      "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear", "wq_fp8_linear",
-                     "wq_read_stream"):
+                     "wq_read_stream", "wq_mx_quantize_act", "wq_mx_linear", "wq_mxfp4_dynamic_linear"):
             getattr(L, name).restype = I
         if L.wq_abi_version() != 1:
             raise RuntimeError("libwq ABI version mismatch")
@@ -178,6 +183,28 @@ def wq_fp8_linear(Xq, act_scale, Wq, w_scale, bias, Y, workspace=None):
                                _ptr(workspace), ws_bytes, _stream(Xq.device)), "wq_fp8_linear")
 
 
+def wq_mx_quantize_act(X, Xq, Xs):
+    M, K = X.shape
+    _check(lib().wq_mx_quantize_act(_ptr(X), M, K, _ptr(Xq), _ptr(Xs), _stream(X.device)), "wq_mx_quantize_act")
+
+
+def wq_mx_linear(Xq, Xs, K, Wq, Ws, bias, N, Y):
+    M = Xq.shape[0]
+    _check(lib().wq_mx_linear(_ptr(Xq), _ptr(Xs), M, K, _ptr(Wq), _ptr(Ws), _ptr(bias), N, _ptr(Y),
+                              _stream(Xq.device)), "wq_mx_linear")
+
+
+def wq_mxfp4_dynamic_workspace(M, K):
+    return lib().wq_mxfp4_dynamic_workspace(M, K)
+
+
+def wq_mxfp4_dynamic_linear(X, Wq, Ws, bias, N, Y, workspace):
+    M, K = X.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().wq_mxfp4_dynamic_linear(_ptr(X), M, K, _ptr(Wq), _ptr(Ws), _ptr(bias), N, _ptr(Y),
+                                         _ptr(workspace), ws_bytes, _stream(X.device)), "wq_mxfp4_dynamic_linear")
+
+
 def wq_read_stream_words(nbytes):
     return lib().wq_read_stream_words(nbytes)
 
@@ -269,6 +296,27 @@ def static_fp8_linear(X, act_scale, Wq, w_scale, bias=None, out=None):
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     ws = workspace(wq_fp8_static_workspace(M, N, K), X.device)
     wq_fp8_static_linear(X, act_scale, Wq, w_scale, bias, out, ws)
+    return out
+
+
+def mx_quantize_act(X):
+    """Dynamic MX quantization of bf16 X [M, K] -> (packed codes [M, K/2], E8M0 scales [M, K/32])."""
+    M, K = X.shape
+    Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    Xs = torch.empty((M, K // 32), dtype=torch.uint8, device=X.device)
+    wq_mx_quantize_act(X, Xq, Xs)
+    return Xq, Xs
+
+
+def mxfp4_dynamic_linear(X, q, bias=None, out=None):
+    """Y = MX(X) . deq(W)^T (+ bias) on the scaled fp4 matrix cores; `q` is a
+    ``quantize("mxfp4", W)`` result."""
+    M, K = X.shape
+    N = q["N"]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    ws = workspace(wq_mxfp4_dynamic_workspace(M, K), X.device)
+    wq_mxfp4_dynamic_linear(X, q["packed"], q["scales"], bias, N, out, ws)
     return out
 
 
