@@ -31,7 +31,7 @@ constexpr int kBK = 64;  // K elements per step
 // smaller tiles, used when there are few tiles, keep four.
 template <int BM, int BN>
 constexpr int tile_stages() {
-  return (BM == 128 && BN == 128) ? 2 : 4;
+  return (BM >= 128 && BN >= 128) ? 2 : 4;
 }
 
 template <int F>
@@ -106,29 +106,33 @@ constexpr int decoded_bytes() {
   return (F == KF_INT4 || F == KF_NVFP4 || F == KF_MXFP4) ? 64 : ((F == KF_FP8) ? 32 : 16);
 }
 
-template <int F, int BM, int BN, int STG, int KS>
-__global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
+// WGN: waves along N in a 2 x WGN wave grid (GT = 128 * WGN threads per K
+// group); each wave owns a (BM/2) x (BN/WGN) block of the tile.
+template <int F, int BM, int BN, int STG, int KS, int WGN>
+__global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   using TF = TileFmt<F>;
-  constexpr int TM = BM / 32, TN = BN / 32;  // 16x16 tiles per wave (waves 2 x 2)
+  constexpr int GT = 128 * WGN;                // threads per K group
+  constexpr int WBN = BN / WGN;                // columns per wave
+  constexpr int TM = BM / 32, TN = WBN / 16;   // 16x16 tiles per wave
   constexpr int LA = kBK * TF::XB / 16;       // 16-byte chunks per activation row per step
-  constexpr int NA = BM * LA / 256;           // activation loads per thread per step
+  constexpr int NA = BM * LA / GT;            // activation loads per thread per step
   constexpr int LB = TF::WSTEP / 16;          // 16-byte chunks per weight column per step
   constexpr int CB = BN * LB;                 // weight chunks per step
-  constexpr int NB = (CB + 255) / 256;        // weight loads per thread per step
+  constexpr int NB = (CB + GT - 1) / GT;      // weight loads per thread per step
   constexpr int DB = decoded_bytes<F>();
-  static_assert(NA * 256 == BM * LA, "activation tile must split evenly over 256 threads");
+  static_assert(NA * GT == BM * LA, "activation tile must split evenly over the group's threads");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // KS groups of 4 waves split K inside the workgroup: group kg owns a
   // contiguous range of K steps and its own double-buffered tiles; all groups
   // step in lockstep (one workgroup barrier per step) and are summed through
   // LDS at the end.
-  const int kg = (int)threadIdx.x >> 8;
+  const int kg = (int)threadIdx.x / GT;
   unsigned char* As = smem + kg * tile_smem<F, BM, BN>();  // [2][BM][ARS]
   unsigned char* Bs = As + 2 * BM * TF::ARS;                // [2][BN][BRS]
 
-  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+  const int tid = (int)threadIdx.x % GT, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int M = a.M, N = a.N, K = a.K;
 
   // XCD-aware tile order: consecutive workgroups go round-robin to the 8 XCDs;
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
   auto gload = [&](int kt, u32x4 (&xa)[NA], u32x4 (&wb)[NB], uint32_t (&sb)[NB]) {
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
-      const int row = q * (256 / LA) + tid / LA;
+      const int row = q * (GT / LA) + tid / LA;
       const int kx = kbeg + kt * kBK + (tid % LA) * (16 / TF::XB);
       xa[q] = bload128(Xr, off_if(kx < kend, ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)kx) * (uint32_t)TF::XB));
     }
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
     for (int q = 0; q < NB; ++q) {
       // threads beyond the chunk count repeat a chunk (identical bytes): no
       // divergent branch, which would make the compiler drain every load
-      const int id = (q * 256 + tid) % CB;
+      const int id = (q * GT + tid) % CB;
       const int col = id / LB, part = id % LB;
       const uint32_t n = (uint32_t)(n0 + col);
       // K elements per 16-byte chunk: 4-bit 32, FP8 16, BF16 8; k0 is the chunk's first K
@@ -194,12 +198,12 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
     unsigned char* B = Bs + buf * BN * TF::BRS;
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
-      const int row = q * (256 / LA) + tid / LA;
+      const int row = q * (GT / LA) + tid / LA;
       *reinterpret_cast<u32x4*>(A + row * TF::ARS + TF::pos(row, tid % LA) * 16) = xa[q];
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      const int id = (q * 256 + tid) % CB;
+      const int id = (q * GT + tid) % CB;
       const int col = id / LB, part = id % LB;
       decode_store<F>(B + col * TF::BRS, col, part * (DB / 16), wb[q], sb[q]);
     }
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
   uint32_t bias_bits[TN], cs_bits[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const uint32_t n = (uint32_t)(n0 + wn * (BN / 2) + 16 * t + c);
+    const uint32_t n = (uint32_t)(n0 + wn * WBN + 16 * t + c);
     bias_bits[t] = bload16(Br, n * 2u);
     cs_bits[t] = (F == KF_FP8 || F == KF_FP8S) ? bload32(Sr, n * 4u) : 0x3F800000u;
   }
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
-        const int r = wn * (BN / 2) + 16 * t + c;
+        const int r = wn * WBN + 16 * t + c;
         bf[t] = *reinterpret_cast<const u32x4*>(B + r * TF::BRS + TF::pos(r, g) * 16);
       }
 #pragma unroll
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
-          const int r = wn * (BN / 2) + 16 * t + c;
+          const int r = wn * WBN + 16 * t + c;
           bf[t] = *reinterpret_cast<const bf16x8*>(B + r * TF::BRS + TF::pos(r, 4 * kk + g) * 16);
         }
 #pragma unroll
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t)
-          *reinterpret_cast<f32x4*>(red + ((((kg - 1) * 4 + wave) * TM * TN + i * TN + t) * 64 + lane) * 4) = acc[i][t];
+          *reinterpret_cast<f32x4*>(red + ((((kg - 1) * (2 * WGN) + wave) * TM * TN + i * TN + t) * 64 + lane) * 4) = acc[i][t];
     }
     __syncthreads();
     if (kg > 0) return;
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
-          const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((((g2 - 1) * 4 + wave) * TM * TN + i * TN + t) * 64 + lane) * 4);
+          const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((((g2 - 1) * (2 * WGN) + wave) * TM * TN + i * TN + t) * 64 + lane) * 4);
           acc[i][t] += o;
         }
   }
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
   if constexpr (F == KF_FP8S) s1 = a.act_scale[0];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + wn * (BN / 2) + 16 * t + c;
+    const int n = n0 + wn * WBN + 16 * t + c;
     const float bias = bitsf(bias_bits[t] << 16);
     const float cs = bitsf(cs_bits[t]);
 #pragma unroll
@@ -347,17 +351,17 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_tiled(LinearArgs a) {
   }
 }
 
-template <int F, int BM, int BN, int KS>
+template <int F, int BM, int BN, int KS, int WGN = 2>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   constexpr int sm = KS * tile_smem<F, BM, BN>();
   static_assert(sm <= 160 * 1024, "tile exceeds the LDS of a CU");
   static_assert(KS == 1 || (KS - 1) * BM * BN * 4 <= sm, "group partials must fit in the tile buffers");
   static std::atomic<int> done{0};
-  auto k = k_gemm_tiled<F, BM, BN, tile_stages<BM, BN>(), KS>;
+  auto k = k_gemm_tiled<F, BM, BN, tile_stages<BM, BN>(), KS, WGN>;
   hipError_t e = allow_smem(k, sm, done);
   if (e != hipSuccess) return e;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
-  k<<<grid, 256 * KS, sm, s>>>(a);
+  k<<<grid, 128 * WGN * KS, sm, s>>>(a);
   return hipGetLastError();
 }
 
@@ -365,6 +369,9 @@ template <int F>
 hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   // 128 x 128 tiles are planned only when there are enough of them (no K
   // groups); the other shapes run with one or two K groups
+  if constexpr (F == KF_MXFP4 || F == KF_FP8 || F == KF_FP8S) {
+    if (p.bm == 256) return launch_tile<F, 256, 256, 1, 4>(a, s);
+  }
   if (p.bm == 128 && p.bn == 128) return launch_tile<F, 128, 128, 1>(a, s);
   if (p.bm == 128) return p.ks >= 2 ? launch_tile<F, 128, 64, 2>(a, s) : launch_tile<F, 128, 64, 1>(a, s);
   if (p.bn == 128) return p.ks >= 2 ? launch_tile<F, 64, 128, 2>(a, s) : launch_tile<F, 64, 128, 1>(a, s);

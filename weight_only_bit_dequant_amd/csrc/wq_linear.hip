@@ -434,8 +434,13 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
     p.S = 1;
     p.bm = 64;
     p.bn = 64;
-    const int cand[3][2] = {{128, 128}, {128, 64}, {64, 128}};
+    // 256 x 256 tiles (8 waves) only where the decode is light enough to fit
+    // the registers of two waves per SIMD without spilling (MXFP4, FP8, E4M3
+    // x E4M3); the INT4 and NVFP4 decodes spill there and run 128 x 128.
+    const bool big_ok = kfmt == KF_MXFP4 || kfmt == KF_FP8 || kfmt == KF_FP8S;
+    const int cand[4][2] = {{256, 256}, {128, 128}, {128, 64}, {64, 128}};
     for (const auto& cb : cand) {
+      if (cb[0] == 256 && !big_ok) continue;
       const int64_t tiles = ((M + cb[0] - 1) / cb[0]) * ((N + cb[1] - 1) / cb[1]);
       if (tiles >= 192) {
         p.bm = cb[0];
@@ -450,7 +455,9 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
     const int64_t steps = (K + 63) / 64;
     p.ks = 1;
-    if (!(p.bm == 128 && p.bn == 128) && tiles <= 512 && steps >= 16) p.ks = 2;
+    if (p.bm < 128 || p.bn < 128) {
+      if (tiles <= 512 && steps >= 16) p.ks = 2;
+    }
     p.part_bytes = 0;
     p.ws_bytes = 0;
     return p;
