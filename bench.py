@@ -62,6 +62,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true", help="skip the M sweep (MXFP4 M=1..4096, static FP8 M=4096)")
     p.add_argument("--trace-summary", metavar="DIR", help="summarize a rocprofv3 --kernel-trace directory")
+    p.add_argument("--pmc-summary", metavar="DIR", help="summarize a rocprofv3 --pmc directory (mean per kernel)")
     p.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarize two rocprofv3 --pmc directories (FETCH_SIZE, WRITE_SIZE)")
     p.add_argument("--sweep-only", action="store_true", help="only the M sweep (e.g. for counter runs at large M)")
@@ -525,11 +526,29 @@ def counters_summary(fetch_dir, write_dir, cmd):
     return text
 
 
+def pmc_summary(d, cmd):
+    """Mean of every collected counter per kernel name."""
+    import numpy as np
+
+    vals = {}
+    for r in _rows(d, "counter_collection.csv"):
+        vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in vals.values() for c in v})
+    lines = ["| kernel | dispatches | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    for k, v in sorted(vals.items()):
+        n = max(len(x) for x in v.values())
+        lines.append("| `%s` | %d | %s |" % (_short(k), n, " | ".join(
+            "%.2f" % float(np.mean(v[c])) if c in v else "" for c in names)))
+    return "Command (from /tmp with TMPDIR=/tmp, repo at $R):\n\n```\n%s\n```\n\n%s\n" % (cmd, "\n".join(lines))
+
+
 def main():
     args = parse()
-    if args.trace_summary or args.counters_summary:
+    if args.trace_summary or args.counters_summary or args.pmc_summary:
         if args.trace_summary:
             text = trace_summary(args.trace_summary, args.cmd)
+        elif args.pmc_summary:
+            text = pmc_summary(args.pmc_summary, args.cmd)
         else:
             text = counters_summary(args.counters_summary[0], args.counters_summary[1], args.cmd)
         if args.title:
