@@ -161,28 +161,32 @@ __global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
 // multiples, or too long for LDS) every step loads 4 scale bytes per row;
 // those loads touch a different row per lane and were measured to dominate
 // the step time when they are used.
-template <int BM, int BN>
+template <int BM, int BN, int GT>
 struct MxTile {
   static constexpr int ROWB = 64;                       // packed bytes of one row per step
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   static constexpr int AS_BYTES = BM * 4, BS_BYTES = BN * 4;  // per-step scale planes (no PRE)
   static constexpr int BUF = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
   static constexpr int TILES = 2 * BUF;
-  static constexpr int NA = BM * 4 / 256, NB = BN * 4 / 256;  // 16-byte chunks per thread
+  static constexpr int NA = BM * 4 / GT, NB = BN * 4 / GT;  // 16-byte chunks per thread
   __device__ static __forceinline__ int pos(int r, int k) { return k ^ ((r >> 1) & 3); }
   // LDS for the whole-K scale rows (PRE)
   static size_t pre_bytes(int K) { return (size_t)(BM + BN) * (size_t)(K / 32); }
 };
 
-template <int BM, int BN, bool PRE>
-__global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
-  using TT = MxTile<BM, BN>;
-  constexpr int TM = BM / 32, TN = BN / 32;
-  static_assert(TT::NA >= 1 && TT::NB >= 1, "tile rows must cover the 256 threads");
+// WGN waves along N (2 x WGN wave grid, GT = 128 * WGN threads); each wave
+// owns a (BM/2) x (BN/WGN) block.
+template <int BM, int BN, int WGN, bool PRE>
+__global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
+  constexpr int GT = 128 * WGN, WBN = BN / WGN;
+  using TT = MxTile<BM, BN, GT>;
+  constexpr int TM = BM / 32, TN = WBN / 16;
+  static_assert(TT::NA >= 1 && TT::NB >= 1 && TT::NA * GT == BM * 4 && TT::NB * GT == BN * 4,
+                "tile rows must split evenly over the threads");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int M = a.M, N = a.N, K = a.K;
 
   // XCD-aware tile order (see the bf16 tiled kernel)
@@ -205,9 +209,9 @@ __global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
     // rows m0 .. m0+BM-1 of the scale matrix are one contiguous byte range;
     // 16-byte chunks, rows past M / N read zero
     const int xchunks = BM * (int)srow / 16, wchunks = BN * (int)srow / 16;
-    for (int q = tid; q < xchunks; q += 256)
+    for (int q = tid; q < xchunks; q += GT)
       *reinterpret_cast<u32x4*>(XS + 16 * q) = bload128(Xsr, (uint32_t)m0 * srow + 16u * q);
-    for (int q = tid; q < wchunks; q += 256)
+    for (int q = tid; q < wchunks; q += GT)
       *reinterpret_cast<u32x4*>(WS + 16 * q) = bload128(Wsr, (uint32_t)n0 * srow + 16u * q);
   }
 
@@ -218,13 +222,13 @@ __global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
     const uint32_t kb = (uint32_t)kt * 64u;  // byte offset of the step in a packed row
 #pragma unroll
     for (int q = 0; q < TT::NA; ++q) {
-      const int id = q * 256 + tid, row = id >> 2, part = id & 3;
+      const int id = q * GT + tid, row = id >> 2, part = id & 3;
       const bool ok = kt * 128 + part * 32 < K;
       xa[st][q] = bload128(Xr, off_if(ok, (uint32_t)(m0 + row) * rowb + kb + 16u * part));
     }
 #pragma unroll
     for (int q = 0; q < TT::NB; ++q) {
-      const int id = q * 256 + tid, row = id >> 2, part = id & 3;
+      const int id = q * GT + tid, row = id >> 2, part = id & 3;
       const bool ok = kt * 128 + part * 32 < K;
       wb[st][q] = bload128(Wr, off_if(ok, (uint32_t)(n0 + row) * rowb + kb + 16u * part));
     }
@@ -245,12 +249,12 @@ __global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
     unsigned char* B = A + TT::A_BYTES;
 #pragma unroll
     for (int q = 0; q < TT::NA; ++q) {
-      const int id = q * 256 + tid, row = id >> 2, part = id & 3;
+      const int id = q * GT + tid, row = id >> 2, part = id & 3;
       *reinterpret_cast<u32x4*>(A + row * TT::ROWB + TT::pos(row, part) * 16) = xa[st][q];
     }
 #pragma unroll
     for (int q = 0; q < TT::NB; ++q) {
-      const int id = q * 256 + tid, row = id >> 2, part = id & 3;
+      const int id = q * GT + tid, row = id >> 2, part = id & 3;
       *reinterpret_cast<u32x4*>(B + row * TT::ROWB + TT::pos(row, part) * 16) = wb[st][q];
     }
     if constexpr (!PRE) {
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
 
   uint32_t bias_bits[TN];
 #pragma unroll
-  for (int t = 0; t < TN; ++t) bias_bits[t] = bload16(Br, (uint32_t)(n0 + wn * (BN / 2) + 16 * t + c) * 2u);
+  for (int t = 0; t < TN; ++t) bias_bits[t] = bload16(Br, (uint32_t)(n0 + wn * WBN + 16 * t + c) * 2u);
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const int r = wn * (BN / 2) + 16 * t + c;
+      const int r = wn * WBN + 16 * t + c;
       bf[t] = *reinterpret_cast<const u32x4*>(B + r * TT::ROWB + TT::pos(r, g) * 16);
       bs[t] = PRE ? ((4 * kt + g < (int)srow) ? WS[r * srow + min(4 * kt + g, (int)srow - 1)] : 127u) : BS[g * BN + r];
     }
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
 
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + wn * (BN / 2) + 16 * t + c;
+    const int n = n0 + wn * WBN + 16 * t + c;
     const float bias = bitsf(bias_bits[t] << 16);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -338,24 +342,29 @@ __global__ __launch_bounds__(256) void k_mx_gemm_tiled(LinearArgs a) {
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGN = 2>
 hipError_t launch_mx_tile(const LinearArgs& a, hipStream_t s) {
-  using TT = MxTile<BM, BN>;
+  using TT = MxTile<BM, BN, 128 * WGN>;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
   const size_t pre = TT::pre_bytes(a.K);
-  if ((a.K / 32) % 16 == 0 && TT::TILES + pre <= 96 * 1024) {
+  constexpr int limit = 128 * 1024;
+  if ((a.K / 32) % 16 == 0 && TT::TILES + pre <= (size_t)limit) {
     static std::atomic<int> done{0};
     const int sm = (int)(TT::TILES + pre);
-    auto k = k_mx_gemm_tiled<BM, BN, true>;
+    auto k = k_mx_gemm_tiled<BM, BN, WGN, true>;
     if (sm > 65536 && !done.load(std::memory_order_acquire)) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         96 * 1024);
+                                         limit);
       if (e != hipSuccess) return e;
       done.store(1, std::memory_order_release);
     }
-    k<<<grid, 256, sm, s>>>(a);
+    k<<<grid, 128 * WGN, sm, s>>>(a);
   } else {
-    k_mx_gemm_tiled<BM, BN, false><<<grid, 256, TT::TILES, s>>>(a);
+    static std::atomic<int> done{0};
+    auto k = k_mx_gemm_tiled<BM, BN, WGN, false>;
+    hipError_t e = allow_smem(k, TT::TILES, done);
+    if (e != hipSuccess) return e;
+    k<<<grid, 128 * WGN, TT::TILES, s>>>(a);
   }
   return hipGetLastError();
 }
@@ -370,8 +379,11 @@ hipError_t launch_mx_quantize_act(const uint16_t* X, int64_t M, int64_t K, uint8
 
 hipError_t launch_mx_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M > 64) {
-    // matrix-core bound: tiles of 128 x 128 when they fill the chip, else 64 x 64
+    // matrix-core bound: 128 x 128 tiles when they fill the chip, else 64 x 64
+    // (measured: 128 x 256 tiles of 8 waves ran no faster at M = 4096, and
+    // 256 x 256 spilled registers)
     const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+
     return t128 >= 192 ? launch_mx_tile<128, 128>(a, s) : launch_mx_tile<64, 64>(a, s);
   }
   const int gx = (a.N + 15) / 16;
