@@ -78,6 +78,53 @@ def dequant_int4(codes, scales_bf16, group=INT4_GROUP):
     return c * np.repeat(s, group, axis=1)
 
 
+def quantize_int4_asym(W_bf16, group=INT4_GROUP):
+    """Asymmetric group-wise INT4 with a zero-point ("TorchAO INT4 Weight-Only
+    Quantization (Linear)", intro: TorchAO's default int4 weight-only scheme is
+    asymmetric, with a nonzero zero-point; the page's own target rejects it and
+    uses the symmetric form instead).
+
+    Readings where the page is silent (the usual affine uint4 scheme, groups as
+    in the symmetric form): per group of `group` consecutive K of one row,
+    lo = min(min w, 0) and hi = max(max w, 0) (the range keeps 0 exactly
+    representable); s = bf16(fp32(fp32(hi - lo) / 15)); zero-point
+    z = clamp(round_half_even(fp32(-lo / s)), 0, 15); code =
+    clamp(round_half_even(fp32(w / s)) + z, 0, 15); dequantized value
+    (code - z) * s.  An all-zero group has s = 0, z = 0 and codes 0.
+
+    Returns (codes uint8 [N, K] in 0..15, scales bf16 uint16 [N, K/group],
+    zero-points uint8 [N, K/group]).
+    """
+    w = bf16_to_f32(W_bf16)
+    N, K = w.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    wg = w.reshape(N, K // group, group)
+    lo = np.minimum(wg.min(axis=2), F32(0.0))
+    hi = np.maximum(wg.max(axis=2), F32(0.0))
+    s_bf16 = f32_to_bf16(_div32((hi - lo).astype(F32), F32(15.0)))
+    s = bf16_to_f32(s_bf16)
+    pos = s > 0
+    z = np.where(pos, np.clip(np.rint(_div32(-lo, s)), 0, 15), 0).astype(np.int64)
+    q = np.where(pos[..., None], np.rint(_div32(wg, s[..., None])), 0).astype(np.int64)
+    codes = np.clip(q + z[..., None], 0, 15).astype(np.uint8).reshape(N, K)
+    return codes, s_bf16, z.astype(np.uint8)
+
+
+def dequant_int4_asym(codes, scales_bf16, zeros, group=INT4_GROUP):
+    """fp64 dequantized weight: (code - z) * s (exact)."""
+    c = np.asarray(codes, np.int64)
+    z = np.repeat(np.asarray(zeros, np.int64), group, axis=1)
+    s = np.repeat(bf16_to_f32(scales_bf16).astype(np.float64), group, axis=1)
+    return (c - z) * s
+
+
+def int4_asym_scale_words(scales_bf16, zeros):
+    """The library's storage of one group's scale and zero-point: a 32-bit
+    word, bf16 scale in bits 0-15 and the zero-point in bits 16-19."""
+    return np.asarray(scales_bf16, np.uint32) | (np.asarray(zeros, np.uint32) << 16)
+
+
 # ------------------------------------------------------------------ FP8 row
 
 
@@ -238,6 +285,7 @@ def dequant_bf16(fmt, codes, scales, g=None):
     kernels).  Definition: evaluate the scale product in fp32 in the order
     code * block-scale (* global), then round once more to bf16:
       int4  : bf16(code * s)                    (exact in fp32)
+      int4_asym : bf16((code - z) * s)          (exact in fp32)
       fp8   : bf16(fp32(dec(code) * s))
       nvfp4 : bf16(fp32(fp32(dec(code) * dec(sc)) * g))
       mxfp4 : bf16(fp32(dec(code) * 2^e))
@@ -245,6 +293,11 @@ def dequant_bf16(fmt, codes, scales, g=None):
     if fmt == "int4":
         c = int4_decode(codes).astype(F32)
         s = np.repeat(bf16_to_f32(scales), codes.shape[1] // scales.shape[1], axis=1)
+        return f32_to_bf16(_mul32(c, s))
+    if fmt == "int4_asym":
+        sc, z = scales
+        c = (np.asarray(codes, np.int64) - np.repeat(np.asarray(z, np.int64), INT4_GROUP, axis=1)).astype(F32)
+        s = np.repeat(bf16_to_f32(sc), INT4_GROUP, axis=1)
         return f32_to_bf16(_mul32(c, s))
     if fmt == "fp8":
         c = e4m3_decode(codes).astype(F32)
@@ -265,6 +318,9 @@ def quantize(fmt, W_bf16):
     if fmt == "int4":
         c, s = quantize_int4_sym(W_bf16)
         return c, s, None
+    if fmt == "int4_asym":
+        c, s, z = quantize_int4_asym(W_bf16)
+        return c, (s, z), None
     if fmt == "fp8":
         c, s = quantize_fp8_row(W_bf16)
         return c, s, None
@@ -280,6 +336,8 @@ def dequant(fmt, codes, scales, g=None):
     """Exact fp64 dequantized weight [N, K]."""
     if fmt == "int4":
         return dequant_int4(codes, scales)
+    if fmt == "int4_asym":
+        return dequant_int4_asym(codes, scales[0], scales[1])
     if fmt == "fp8":
         return dequant_fp8_row(codes, scales)
     if fmt == "nvfp4":
