@@ -39,6 +39,14 @@
  *            E4M3 block scales uint8 [N][K/16], one fp32 global scale
  *   WQ_MXFP4 E2M1 codes [N][K], packed [N][K/2], E8M0 block scales
  *            uint8 [N][K/32]
+ *   WQ_INT4_ASYM asymmetric group-wise INT4 ("TorchAO INT4 Weight-Only
+ *            Quantization (Linear)", intro: TorchAO's default scheme, with a
+ *            nonzero zero-point), group 128 along K: codes uint8 [N][K]
+ *            (0..15), packed [N][K/2]; per group one uint32 word: bf16 scale
+ *            in bits 0-15, zero-point in bits 16-19 -> scales uint32
+ *            [N][K/128].  s = bf16((hi - lo) / 15) with lo = min(min w, 0),
+ *            hi = max(max w, 0); z = clamp(rint(-lo / s), 0, 15); code =
+ *            clamp(rint(w / s) + z, 0, 15); value (code - z) * s.
  * Packing: byte j of a packed row holds element 2j in its low nibble and
  * element 2j+1 in its high nibble.
  */
@@ -59,7 +67,8 @@ typedef enum wq_format {
   WQ_INT4 = 1,
   WQ_FP8 = 2,
   WQ_NVFP4 = 3,
-  WQ_MXFP4 = 4
+  WQ_MXFP4 = 4,
+  WQ_INT4_ASYM = 5
 } wq_format;
 
 typedef enum wq_status {

@@ -44,10 +44,11 @@ def test_layout_sizes():
     assert wq.wq_layout("nvfp4", 4096, 3072) == (4096 * 3072, 4096 * 1536, 4096 * 192, 4)
     assert wq.wq_layout("mxfp4", 4096, 3072) == (4096 * 3072, 4096 * 1536, 4096 * 96, 0)
     assert wq.wq_layout("bf16", 8, 16) == (256, 256, 0, 0)
+    assert wq.wq_layout("int4_asym", 4096, 3072) == (4096 * 3072, 4096 * 1536, 4096 * 24 * 4, 0)
 
 
 @pytest.mark.parametrize("fmt,N,K", [("int4", 64, 100), ("nvfp4", 40, 64), ("nvfp4", 64, 40), ("mxfp4", 48, 64),
-                                     ("mxfp4", 64, 48)])
+                                     ("mxfp4", 64, 48), ("int4_asym", 64, 192)])
 def test_shape_rules(fmt, N, K):
     with pytest.raises(ValueError) as e:
         wq.wq_layout(fmt, N, K)

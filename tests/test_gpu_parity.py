@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 REL_TOL = 1e-2
-FMTS = ["int4", "fp8", "nvfp4", "mxfp4"]
+FMTS = ["int4", "fp8", "nvfp4", "mxfp4", "int4_asym"]
 
 
 def dev_bf16(bits):
@@ -53,6 +53,8 @@ def check_quant_exact(fmt, W_bits, q):
     assert np.array_equal(gc.astype(np.int64), codes.astype(np.int64)), f"{fmt} codes differ"
     if fmt == "int4":
         assert np.array_equal(host(q["scales"].view(torch.int16)).view(np.uint16), scales)
+    elif fmt == "int4_asym":
+        assert np.array_equal(host(q["scales"]).view(np.uint32), Q.int4_asym_scale_words(*scales))
     elif fmt == "fp8":
         assert np.array_equal(host(q["scales"]).view(np.uint32), scales.view(np.uint32))
     else:
@@ -132,7 +134,7 @@ def test_linear_small_shapes(fmt, M, N, K):
     assert_close(Y, oracle_linear(fmt, W, b, X), f"{fmt} M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("fmt,N", [("int4", 200), ("fp8", 200), ("nvfp4", 208), ("mxfp4", 224)])
+@pytest.mark.parametrize("fmt,N", [("int4", 200), ("fp8", 200), ("nvfp4", 208), ("mxfp4", 224), ("int4_asym", 200)])
 def test_linear_ragged_n(fmt, N):
     # column tail that does not fill the 64-column workgroup tile
     W, b, X = synth.linear_case(N, 256, 5, cfg=33)
@@ -187,7 +189,7 @@ TILED_CASES = [(256, 1024, 2176), (256, 1024, 2112), (640, 2048, 1152), (384, 40
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", TILED_CASES)
 def test_linear_tiled_k_groups(fmt, M, N, K):
-    if fmt == "int4" and K % 128:
+    if fmt in ("int4", "int4_asym") and K % 128:
         pytest.skip("INT4 groups need K % 128 == 0")
     W, b, X = synth.linear_case(N, K, M, cfg=80 + M % 7)
     _, Y = run_linear(fmt, W, b, X)

@@ -41,17 +41,23 @@ const char* fmt_name(int f) {
     case WQ_FP8: return "FP8";
     case WQ_NVFP4: return "NVFP4";
     case WQ_MXFP4: return "MXFP4";
+    case WQ_INT4_ASYM: return "INT4_ASYM";
     default: return "?";
   }
 }
 
-bool valid_fmt(int f) { return f >= WQ_BF16 && f <= WQ_MXFP4; }
+bool valid_fmt(int f) { return f >= WQ_BF16 && f <= WQ_INT4_ASYM; }
+
+// Kernel-side format id (the public ids coincide with the kernels' except the
+// asymmetric INT4, whose kernel id follows the static-FP8 GEMM's).
+int kfmt_of(int f) { return f == WQ_INT4_ASYM ? wq::KF_INT4A : f; }
 
 // Divisibility rules of each format (INT4: group 128 along K; NVFP4: last two
 // weight dims % 16; MXFP4: K and N % 32).
 wq_status check_shape_rule(int f, int64_t N, int64_t K) {
   if (N < 0 || K < 0) return fail(WQ_EINVAL, "negative size N=%lld K=%lld", (long long)N, (long long)K);
-  if (f == WQ_INT4 && K % 128) return fail(WQ_ESHAPE, "INT4 needs K %% 128 == 0 (K=%lld)", (long long)K);
+  if ((f == WQ_INT4 || f == WQ_INT4_ASYM) && K % 128)
+    return fail(WQ_ESHAPE, "INT4 needs K %% 128 == 0 (K=%lld)", (long long)K);
   if (f == WQ_NVFP4 && (N % 16 || K % 16))
     return fail(WQ_ESHAPE, "NVFP4 needs N %% 16 == 0 and K %% 16 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
   if (f == WQ_MXFP4 && (N % 32 || K % 32))
@@ -106,6 +112,7 @@ wq_status wq_layout(int fmt, int64_t N, int64_t K, size_t* codes_bytes, size_t* 
     case WQ_FP8: cb = pb = nk; sb = (size_t)N * 4; break;
     case WQ_NVFP4: cb = nk; pb = nk / 2; sb = (size_t)N * (size_t)(K / 16); gb = 4; break;
     case WQ_MXFP4: cb = nk; pb = nk / 2; sb = (size_t)N * (size_t)(K / 32); break;
+    case WQ_INT4_ASYM: cb = nk; pb = nk / 2; sb = (size_t)N * (size_t)(K / 128) * 4; break;
   }
   if (codes_bytes) *codes_bytes = cb;
   if (packed_bytes) *packed_bytes = pb;
@@ -125,7 +132,7 @@ wq_status wq_quantize(int fmt, const void* W, int64_t N, int64_t K, void* codes,
   if ((fmt == WQ_NVFP4) != (global_scale != nullptr))
     return fail(WQ_EINVAL, "wq_quantize: global_scale is required for NVFP4 and must be NULL otherwise");
   if (!aligned16(W) || !aligned16(codes)) return fail(WQ_EALIGN, "wq_quantize: W and codes must be 16-byte aligned");
-  return hip_status(wq::launch_quantize(fmt, (const uint16_t*)W, N, K, codes, scales, global_scale,
+  return hip_status(wq::launch_quantize(kfmt_of(fmt), (const uint16_t*)W, N, K, codes, scales, global_scale,
                                         (hipStream_t)stream),
                     "wq_quantize launch");
 }
@@ -141,7 +148,7 @@ wq_status wq_pack(int fmt, const void* codes, int64_t N, int64_t K, void* packed
   const int64_t nk = N * K;
   if (fmt == WQ_FP8 ? (nk % 16) : (nk % 32))
     return fail(WQ_EUNSUPPORTED, "wq_pack: N*K must be a multiple of %d", fmt == WQ_FP8 ? 16 : 32);
-  return hip_status(wq::launch_pack(fmt, (const uint8_t*)codes, N, K, (uint8_t*)packed, (hipStream_t)stream),
+  return hip_status(wq::launch_pack(kfmt_of(fmt), (const uint8_t*)codes, N, K, (uint8_t*)packed, (hipStream_t)stream),
                     "wq_pack launch");
 }
 
@@ -156,14 +163,14 @@ wq_status wq_dequantize(int fmt, const void* packed, const void* scales, const f
   if (fmt == WQ_NVFP4 && !global_scale) return fail(WQ_EINVAL, "wq_dequantize: NVFP4 needs global_scale");
   if (K % 8) return fail(WQ_EUNSUPPORTED, "wq_dequantize: K %% 8 != 0");
   if (!aligned16(packed) || !aligned16(W_out)) return fail(WQ_EALIGN, "wq_dequantize: buffers must be 16-byte aligned");
-  return hip_status(wq::launch_dequantize(fmt, packed, scales, global_scale, N, K, (uint16_t*)W_out,
+  return hip_status(wq::launch_dequantize(kfmt_of(fmt), packed, scales, global_scale, N, K, (uint16_t*)W_out,
                                           (hipStream_t)stream),
                     "wq_dequantize launch");
 }
 
 size_t wq_linear_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
   if (!valid_fmt(fmt) || M <= 0 || N <= 0 || K <= 0) return 0;
-  return wq::plan_linear(fmt, M, N, K).ws_bytes;
+  return wq::plan_linear(kfmt_of(fmt), M, N, K).ws_bytes;
 }
 
 static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int64_t K, const void* W,
@@ -218,7 +225,7 @@ static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int6
 wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* packed, const void* scales,
                     const float* global_scale, const void* bias, int64_t N, void* Y, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  return linear_common(fmt, fmt, X, M, K, packed, scales, global_scale, nullptr, bias, N, Y, workspace,
+  return linear_common(kfmt_of(fmt), fmt, X, M, K, packed, scales, global_scale, nullptr, bias, N, Y, workspace,
                        workspace_bytes, stream);
 }
 

@@ -68,19 +68,22 @@ template <int F>
 __device__ __forceinline__ void decode_store(unsigned char* row, int r, int k0, u32x4 w, uint32_t sc) {
   using TF = TileFmt<F>;
   auto at = [&](int p) { return reinterpret_cast<bf16x8*>(row + TF::pos(r, k0 + p) * 16); };
-  if constexpr (F == KF_INT4) {
+  if constexpr (F == KF_INT4 || F == KF_INT4A) {
+    // signed codes: 136 + code after XOR 8; unsigned: 128 + code, value
+    // (code - z) * s -- both exact in fp32 before the bf16 rounding
     const float s = bitsf(sc << 16);
+    const float bias = (F == KF_INT4) ? 136.f : (float)(128u + ((sc >> 16) & 15u));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // 8 nibbles -> bf16(code * s), K order kept
-      const bf16x8 biased = dec_int4_biased(w[j]);  // 136 + code, exact
+      // 8 nibbles -> bf16(value), K order kept
+      const bf16x8 biased = (F == KF_INT4) ? dec_int4_biased(w[j]) : dec_uint4_biased(w[j]);
       const u32x4 bb = __builtin_bit_cast(u32x4, biased);
       bf16x8 r8;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const float lo = bitsf(bb[p] << 16), hi = bitsf(bb[p] & 0xFFFF0000u);
-        r8[2 * p] = (__bf16)fmaf(lo, s, -136.f * s);
-        r8[2 * p + 1] = (__bf16)fmaf(hi, s, -136.f * s);
+        r8[2 * p] = (__bf16)fmaf(lo, s, -bias * s);
+        r8[2 * p + 1] = (__bf16)fmaf(hi, s, -bias * s);
       }
       *at(j) = r8;
     }
@@ -103,7 +106,7 @@ __device__ __forceinline__ void decode_store(unsigned char* row, int r, int k0, 
 // bytes of decoded operand written per 16-byte packed chunk
 template <int F>
 constexpr int decoded_bytes() {
-  return (F == KF_INT4 || F == KF_NVFP4 || F == KF_MXFP4) ? 64 : ((F == KF_FP8) ? 32 : 16);
+  return (F == KF_INT4 || F == KF_INT4A || F == KF_NVFP4 || F == KF_MXFP4) ? 64 : ((F == KF_FP8) ? 32 : 16);
 }
 
 // WGN: waves along N in a 2 x WGN wave grid (GT = 128 * WGN threads per K
@@ -149,6 +152,7 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * (uint32_t)K * (uint32_t)TF::XB);
   uint32_t sbytes = 0;
   if constexpr (F == KF_INT4) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 2u;
+  else if constexpr (F == KF_INT4A) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 4u;
   else if constexpr (F == KF_NVFP4) sbytes = (uint32_t)N * (uint32_t)(K / 16);
   else if constexpr (F == KF_MXFP4) sbytes = (uint32_t)N * (uint32_t)(K / 32);
   else if constexpr (F == KF_FP8 || F == KF_FP8S) sbytes = (uint32_t)N * 4u;
@@ -188,6 +192,7 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
       const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : ((F == KF_FP8 || F == KF_FP8S) ? (uint32_t)k0 : (uint32_t)k0 / 2u);
       wb[q] = bload128(Wr, off_if(ok, n * wrow + byte0));
       if constexpr (F == KF_INT4) sb[q] = bload16(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u));
+      else if constexpr (F == KF_INT4A) sb[q] = bload32(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 4u));
       else if constexpr (F == KF_NVFP4) sb[q] = bload16(Sr, off_if(ok, n * (uint32_t)(K / 16) + (uint32_t)(k0 / 16)));
       else if constexpr (F == KF_MXFP4) sb[q] = bload8(Sr, off_if(ok, n * (uint32_t)(K / 32) + (uint32_t)(k0 / 32)));
       else sb[q] = 0u;
@@ -384,6 +389,7 @@ hipError_t launch_gemm_tiled(int kfmt, const LinearArgs& a, const LinearPlan& p,
   switch (kfmt) {
     case KF_BF16: return launch_tiled_f<KF_BF16>(a, p, s);
     case KF_INT4: return launch_tiled_f<KF_INT4>(a, p, s);
+    case KF_INT4A: return launch_tiled_f<KF_INT4A>(a, p, s);
     case KF_FP8: return launch_tiled_f<KF_FP8>(a, p, s);
     case KF_NVFP4: return launch_tiled_f<KF_NVFP4>(a, p, s);
     case KF_MXFP4: return launch_tiled_f<KF_MXFP4>(a, p, s);

@@ -10,7 +10,7 @@ namespace wq {
 
 // Kernel-side format ids (the ABI's wq_format values plus the FP8-activation
 // variant used by the static path).
-enum KFmt { KF_BF16 = 0, KF_INT4 = 1, KF_FP8 = 2, KF_NVFP4 = 3, KF_MXFP4 = 4, KF_FP8S = 5 };
+enum KFmt { KF_BF16 = 0, KF_INT4 = 1, KF_FP8 = 2, KF_NVFP4 = 3, KF_MXFP4 = 4, KF_FP8S = 5, KF_INT4A = 6 };
 
 // Workspace: split-K partial sums (fp32) when a plan splits K across
 // workgroups; the static path appends its quantized activations.

@@ -35,6 +35,10 @@ template <>
 struct FmtT<KF_FP8S> {
   static constexpr int KPL = 16;
 };
+template <>
+struct FmtT<KF_INT4A> {
+  static constexpr int KPL = 32;
+};
 
 template <int F>
 __device__ __forceinline__ int64_t kbyte(int64_t k) {
@@ -48,6 +52,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // INT4: 8 nibbles (K order 0..7) -> bf16 values 136 + code, K order kept.
 __device__ __forceinline__ bf16x8 dec_int4_biased(uint32_t w) {
   const uint32_t u = w ^ 0x88888888u;
+  const uint32_t v = u >> 4;
+  u32x4 p;
+  p.x = (__builtin_amdgcn_perm(v, u, 0x0C040C00u) & 0x000F000Fu) | 0x43004300u;
+  p.y = (__builtin_amdgcn_perm(v, u, 0x0C050C01u) & 0x000F000Fu) | 0x43004300u;
+  p.z = (__builtin_amdgcn_perm(v, u, 0x0C060C02u) & 0x000F000Fu) | 0x43004300u;
+  p.w = (__builtin_amdgcn_perm(v, u, 0x0C070C03u) & 0x000F000Fu) | 0x43004300u;
+  return as_bf16x8(p);
+}
+
+// Unsigned INT4: 8 nibbles (K order 0..7) -> bf16 values 128 + code.
+__device__ __forceinline__ bf16x8 dec_uint4_biased(uint32_t u) {
   const uint32_t v = u >> 4;
   u32x4 p;
   p.x = (__builtin_amdgcn_perm(v, u, 0x0C040C00u) & 0x000F000Fu) | 0x43004300u;

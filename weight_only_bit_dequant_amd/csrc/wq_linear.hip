@@ -120,6 +120,7 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * (uint32_t)K * (ACT8 ? 1u : 2u));
   uint32_t sbytes = 0;
   if constexpr (F == KF_INT4) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 2u;
+  else if constexpr (F == KF_INT4A) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 4u;
   else if constexpr (F == KF_NVFP4) sbytes = (uint32_t)N * (uint32_t)(K / 16);
   else if constexpr (F == KF_MXFP4) sbytes = (uint32_t)N * (uint32_t)(K / 32);
   else if constexpr (F == KF_FP8 || F == KF_FP8S) sbytes = (uint32_t)N * 4u;
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
         const uint32_t n = (uint32_t)(n0 + 16 * t + c);
         w[st][t] = bload128(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
         if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u));
+        else if constexpr (F == KF_INT4A) sc[st][t] = bload32(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 4u));
         else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, off_if(kv, n * (uint32_t)(K / 16) + (uint32_t)(kl / 16)));
         else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, off_if(kv, n * (uint32_t)(K / 32) + (uint32_t)(kl / 32)));
         else sc[st][t] = 0u;
@@ -201,7 +203,8 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
             xv[st][i][j] = *reinterpret_cast<const u32x4*>(
                 slot + (16 * i + c) * XS::ROWB + XS::pos(16 * i + c, (g * KPL + 8 * j) * XS::XB / 16) * 16);
       }
-      if constexpr (F == KF_INT4) {
+      if constexpr (F == KF_INT4 || F == KF_INT4A) {
+        // bias: 136 for signed codes (XOR 8), 128 + zero-point for unsigned ones
         f32x4 tmp[MT][NTW], rs[MT];
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
         for (int j = 0; j < 4; ++j) {
           bf16x8 b[NTW];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) b[t] = dec_int4_biased(w[st][t][j]);
+          for (int t = 0; t < NTW; ++t) b[t] = (F == KF_INT4) ? dec_int4_biased(w[st][t][j]) : dec_uint4_biased(w[st][t][j]);
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
             const bf16x8 A = as_bf16x8(xv[st][i][j]);
@@ -226,10 +229,11 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
           const float s = bitsf(sc[st][t] << 16);
+          const float nb = (F == KF_INT4) ? -136.f : -(float)(128u + ((sc[st][t] >> 16) & 15u));
 #pragma unroll
           for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(s, fmaf(-136.f, rs[i][r], tmp[i][t][r]), acc[i][t][r]);
+            for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(s, fmaf(nb, rs[i][r], tmp[i][t][r]), acc[i][t][r]);
         }
       } else if constexpr (F == KF_NVFP4) {
 #pragma unroll
@@ -503,6 +507,7 @@ hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hip
   switch (kfmt) {
     case KF_BF16: return launch_f<KF_BF16>(a, p, s);
     case KF_INT4: return launch_f<KF_INT4>(a, p, s);
+    case KF_INT4A: return launch_f<KF_INT4A>(a, p, s);
     case KF_FP8: return launch_f<KF_FP8>(a, p, s);
     case KF_NVFP4: return launch_f<KF_NVFP4>(a, p, s);
     case KF_MXFP4: return launch_f<KF_MXFP4>(a, p, s);

@@ -67,6 +67,51 @@ __global__ __launch_bounds__(kThreads) void k_quant_int4(const uint16_t* __restr
   for (int i = 0; i < 8; ++i) out[i] = u32x4{packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]};
 }
 
+// ---------------------------------------------------------------- INT4, asymmetric
+// The INT4 page's intro names TorchAO's default asymmetric scheme (nonzero
+// zero-point).  Per (row, group of 128 K): lo = min(min w, 0), hi = max(max w,
+// 0), s = bf16((hi - lo) / 15), z = clamp(rint(-lo / s), 0, 15), code =
+// clamp(rint(w / s) + z, 0, 15); the group's word holds s | z << 16.  One
+// thread per (row, group).
+__global__ __launch_bounds__(kThreads) void k_quant_int4a(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint32_t* __restrict__ scales) {
+  const int64_t G = K / 128;
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= N * G) return;
+  const int64_t n = id / G, gi = id % G;
+  const uint16_t* w = W + n * K + gi * 128;
+  float v[128];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load16_bf16(w + 16 * i, v + 16 * i);
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int i = 0; i < 128; ++i) {
+    lo = fminf(lo, v[i]);
+    hi = fmaxf(hi, v[i]);
+  }
+  const uint16_t sb = f32_to_bf16((hi - lo) / 15.0f);
+  const float s = bf16_to_f32(sb);
+  int z = 0;
+  if (s > 0.f) {
+    z = (int)__builtin_rintf(-lo / s);
+    z = z < 0 ? 0 : (z > 15 ? 15 : z);
+  }
+  scales[n * G + gi] = (uint32_t)sb | ((uint32_t)z << 16);
+  uint32_t packed[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) packed[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 128; ++i) {
+    int c = (s > 0.f) ? (int)__builtin_rintf(v[i] / s) + z : 0;
+    c = c < 0 ? 0 : (c > 15 ? 15 : c);
+    packed[i >> 2] |= (uint32_t)c << (8 * (i & 3));
+  }
+  u32x4* out = reinterpret_cast<u32x4*>(codes + n * K + gi * 128);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = u32x4{packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]};
+}
+
 // ---------------------------------------------------------------- FP8 row
 // "TorchAO FP8 Weight-Only Quantization (Linear)": one fp32 scale per output
 // row, s = max|w| / 448.  One workgroup per row.
@@ -239,6 +284,9 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
       if constexpr (F == KF_INT4) {
         const float s = bf16_to_f32(reinterpret_cast<const uint16_t*>(scales)[n * (K / 128) + (k0 + i) / 128]);
         v = (float)((int)c - ((c & 8u) ? 16 : 0)) * s;
+      } else if constexpr (F == KF_INT4A) {
+        const uint32_t sw = reinterpret_cast<const uint32_t*>(scales)[n * (K / 128) + (k0 + i) / 128];
+        v = (float)((int)c - (int)((sw >> 16) & 15u)) * bitsf(sw << 16);
       } else if constexpr (F == KF_NVFP4) {
         const float d = e4m3_decode(reinterpret_cast<const uint8_t*>(scales)[n * (K / 16) + (k0 + i) / 16]);
         v = (e2m1_decode(c) * d) * gscale[0];
@@ -298,6 +346,9 @@ hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t N, int64_t K, voi
     case KF_INT4:
       k_quant_int4<<<grid_for(N * (K / 128)), kThreads, 0, s>>>(W, N, K, (int8_t*)codes, (uint16_t*)scales);
       break;
+    case KF_INT4A:
+      k_quant_int4a<<<grid_for(N * (K / 128)), kThreads, 0, s>>>(W, N, K, (uint8_t*)codes, (uint32_t*)scales);
+      break;
     case KF_FP8:
       k_quant_fp8row<<<(unsigned)N, kThreads, 0, s>>>(W, K, (uint8_t*)codes, (float*)scales);
       break;
@@ -343,6 +394,7 @@ hipError_t launch_dequantize(int fmt, const void* packed, const void* scales, co
       break;
     }
     case KF_INT4: k_dequant<KF_INT4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_INT4A: k_dequant<KF_INT4A><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
     case KF_FP8: k_dequant<KF_FP8><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
     case KF_NVFP4: k_dequant<KF_NVFP4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
     case KF_MXFP4: k_dequant<KF_MXFP4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;

@@ -35,6 +35,8 @@ WORKLOADS = {
     "nvfp4": dict(fmt="nvfp4", N=LINEAR_N, K=LINEAR_K, M=(32,), bias=True, cfg=3),
     "mxfp4": dict(fmt="mxfp4", N=LINEAR_N, K=LINEAR_K, M=(1, 32, 256, 4096), bias=True, cfg=4),
     "static_fp8": dict(fmt="static_fp8", N=LINEAR_N, K=LINEAR_K, M=(32, 4096), bias=False, cfg=5),
+    # the same layer quantized with the asymmetric INT4 scheme (beside the headline configs)
+    "int4_asym": dict(fmt="int4_asym", N=LINEAR_N, K=LINEAR_K, M=(32,), bias=True, cfg=7),
 }
 
 

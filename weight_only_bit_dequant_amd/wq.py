@@ -16,7 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libwq.so")
 
-FORMATS = {"bf16": 0, "int4": 1, "fp8": 2, "nvfp4": 3, "mxfp4": 4}
+FORMATS = {"bf16": 0, "int4": 1, "fp8": 2, "nvfp4": 3, "mxfp4": 4, "int4_asym": 5}
 OK, EINVAL, ESHAPE, EALIGN, EUNSUPPORTED, EWORKSPACE, EHIP = range(7)
 
 
@@ -244,6 +244,8 @@ def scale_dtype_shape(fmt, N, K):
         return torch.uint8, (N, K // 16)
     if fmt == 4:
         return torch.uint8, (N, K // 32)
+    if fmt == 5:
+        return torch.int32, (N, K // 128)  # uint32 words: bf16 scale | zero-point << 16
     return None, None
 
 
@@ -253,7 +255,7 @@ def quantize(fmt, W):
     f = _fmt(fmt)
     N, K = W.shape
     dev = W.device
-    codes = torch.empty((N, K), dtype=torch.int8 if f == 1 else torch.uint8, device=dev)
+    codes = torch.empty((N, K), dtype=torch.int8 if f == 1 else torch.uint8, device=dev)  # INT4_ASYM: 0..15
     sdt, sshape = scale_dtype_shape(f, N, K)
     scales = torch.empty(sshape, dtype=sdt, device=dev)
     g = torch.empty(1, dtype=torch.float32, device=dev) if f == 3 else None
