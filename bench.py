@@ -250,7 +250,51 @@ def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
                 "launches": 1 if fmt == "mxfp4" else 2,
             }
             del g
+    res.update(mlp2_timing(dev, capture, reps_small))
     return res
+
+
+def mlp2_timing(dev, capture, reps):
+    """The static page's model (32 x 256 -> 512 -> 128, no bias) as one fused
+    kernel and as two unfused static layers (four launches); weights warm."""
+    import torch
+
+    from weight_only_bit_dequant_amd import synth, wq
+
+    W1, W2 = (synth.as_torch_bf16(w, dev) for w in synth.mlp_weights())
+    cal = [synth.as_torch_bf16(b, dev) for b in synth.calibration_batches(32, 256)]
+    s1, _ = wq.calibrate_act_scale(cal)
+    s2, _ = wq.calibrate_act_scale([wq.linear(x, wq.dense(W1)) for x in cal])
+    q1, q2 = wq.quantize("fp8", W1), wq.quantize("fp8", W2)
+    X = synth.as_torch_bf16(synth.activations(32, 256, synth.SEED_X + 5), dev)
+    Y = torch.empty((32, 128), dtype=torch.bfloat16, device=dev)
+
+    def fused(first, count):
+        for _ in range(count):
+            wq.wq_fp8_static_mlp2(X, s1, q1["codes"], q1["scales"], None, s2, q2["codes"], q2["scales"], None, Y)
+
+    H = torch.empty((32, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(max(1, wq.wq_fp8_static_workspace(32, 512, 256), wq.wq_fp8_static_workspace(32, 128, 512)),
+                     dtype=torch.uint8, device=dev)
+
+    def unfused(first, count):
+        for _ in range(count):
+            wq.wq_fp8_static_linear(X, s1, q1["codes"], q1["scales"], None, H, ws)
+            wq.wq_fp8_static_linear(H, s2, q2["codes"], q2["scales"], None, Y, ws)
+
+    out = {}
+    for name, fn, launches in (("static_mlp2_fused_M32", fused, 1), ("static_mlp2_unfused_M32", unfused, 4)):
+        g = capture(fn, reps)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = {"us_per_call": round(a.elapsed_time(b) * 1e3 / reps, 3), "launches": launches}
+        del g
+    return out
 
 
 def main_bench(args):

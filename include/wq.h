@@ -222,6 +222,26 @@ wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_s
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Fused two-layer static-FP8 MLP ("TorchAO Static FP8 Quantization (Linear)",
+ * model and "Calibrate, then insert static FP8 Q/DQ": Linear(K1, N1) ->
+ * Linear(N1, N2), each input quantized with its calibrated act_scale and each
+ * GEMM run in FP8).  Computes, in one kernel,
+ *   H = bf16(Q(X, act_scale1) . deq(W1q)^T * act_scale1 * w1_scale[n] (+ b1))
+ *   Y = bf16(Q(H, act_scale2) . deq(W2q)^T * act_scale2 * w2_scale[n] (+ b2))
+ * with the same per-step arithmetic as two wq_fp8_static_linear calls (results
+ * differ only by fp32 accumulation order); H never leaves the chip.
+ * W1q E4M3 [N1][K1], W2q E4M3 [N2][N1], scales float [N1] / [N2], biases bf16
+ * or NULL.  K1 % 16 == 0, N1 % 16 == 0, and 16 rows of the input and hidden
+ * codes plus both layers' column scales and biases must fit in the 160 KiB LDS
+ * of a CU (K1 + N1 up to about 9.5K; else WQ_EUNSUPPORTED -- use two
+ * wq_fp8_static_linear calls).  No workspace.
+ */
+wq_status wq_fp8_static_mlp2(const void* X, int64_t M, int64_t K1, const float* act_scale1, const void* W1q,
+                             const float* w1_scale, const void* b1, int64_t N1, const float* act_scale2,
+                             const void* W2q, const float* w2_scale, const void* b2, int64_t N2, void* Y,
+                             void* stream);
+
+/*
  * MXFP4 dynamic-activation x MXFP4-weight Linear ("TorchAO MXFP4 Dynamic
  * Activation + MX Weight (Linear)", intro: weights MXFP4, activations
  * quantized to MX on every call, the GEMM on native MXFP4 matrix units).

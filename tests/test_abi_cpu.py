@@ -128,6 +128,14 @@ def test_quantize_pack_dequant_validation():
     assert L.wq_mxfp4_dynamic_linear(v(16), 32, 3072, v(16), v(16), None, 4096, v(16), v(16), need - 1,
                                      None) == wq.EWORKSPACE
     assert L.wq_mxfp4_dynamic_linear(v(16), 0, 3072, v(16), v(16), None, 4096, v(16), None, 0, None) == wq.OK
+    # fused static MLP
+    mlp = lambda M=32, K1=256, N1=512, N2=128, X=16: L.wq_fp8_static_mlp2(
+        v(X), M, K1, v(16), v(16), v(16), None, N1, v(16), v(16), v(16), None, N2, v(16), None)
+    assert mlp(K1=24) == wq.EUNSUPPORTED
+    assert mlp(N1=40) == wq.EUNSUPPORTED
+    assert mlp(K1=8192, N1=4096) == wq.EUNSUPPORTED  # 16 rows exceed the LDS
+    assert mlp(X=8) == wq.EALIGN
+    assert mlp(M=0) == wq.OK
     # read-only stream (measurement aid)
     assert L.wq_read_stream(v(16), 0, None, None) == wq.OK
     assert L.wq_read_stream(None, 64, v(16), None) == wq.EINVAL

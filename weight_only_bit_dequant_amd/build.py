@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 
-SOURCES = ["wq_api.hip", "wq_quant.hip", "wq_linear.hip", "wq_gemm_tiled.hip", "wq_mx.hip"]
+SOURCES = ["wq_api.hip", "wq_quant.hip", "wq_linear.hip", "wq_gemm_tiled.hip", "wq_mx.hip", "wq_mlp.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -372,6 +372,43 @@ wq_status wq_mxfp4_dynamic_linear(const void* X, int64_t M, int64_t K, const voi
   return wq_mx_linear(xq, xs, M, K, Wq, Ws, bias, N, Y, stream);
 }
 
+wq_status wq_fp8_static_mlp2(const void* X, int64_t M, int64_t K1, const float* act_scale1, const void* W1q,
+                             const float* w1_scale, const void* b1, int64_t N1, const float* act_scale2,
+                             const void* W2q, const float* w2_scale, const void* b2, int64_t N2, void* Y,
+                             void* stream) {
+  if (M < 0 || K1 < 0 || N1 < 0 || N2 < 0) return fail(WQ_EINVAL, "negative size");
+  if (M == 0 || N2 == 0) return ok();
+  if (K1 == 0 || N1 == 0) return fail(WQ_EUNSUPPORTED, "K1 == 0 or N1 == 0");
+  if (K1 % 16 || N1 % 16)
+    return fail(WQ_EUNSUPPORTED, "fused MLP needs K1 %% 16 == 0 and N1 %% 16 == 0 (K1=%lld N1=%lld)", (long long)K1,
+                (long long)N1);
+  if (M > kMaxDim || K1 > kMaxDim || N1 > kMaxDim || N2 > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (wq::mlp2_smem_bytes(K1, N1, N2) > (size_t)160 * 1024)
+    return fail(WQ_EUNSUPPORTED, "fused MLP: 16 rows of K1 + N1 codes exceed the LDS of a CU");
+  if (N1 * K1 >= kMaxBufferBytes || N2 * N1 >= kMaxBufferBytes || M * K1 * 2 >= kMaxBufferBytes)
+    return fail(WQ_EUNSUPPORTED, "weight or activation buffer of 2^31 bytes or more");
+  if (!X || !act_scale1 || !W1q || !w1_scale || !act_scale2 || !W2q || !w2_scale || !Y)
+    return fail(WQ_EINVAL, "wq_fp8_static_mlp2: null pointer");
+  if (!aligned16(X) || !aligned16(W1q) || !aligned16(W2q) || !aligned16(Y))
+    return fail(WQ_EALIGN, "X, W1q, W2q and Y must be 16-byte aligned");
+  wq::Mlp2Args a{};
+  a.X = (const uint16_t*)X;
+  a.act_scale1 = act_scale1;
+  a.W1 = (const uint8_t*)W1q;
+  a.w1_scale = w1_scale;
+  a.b1 = (const uint16_t*)b1;
+  a.act_scale2 = act_scale2;
+  a.W2 = (const uint8_t*)W2q;
+  a.w2_scale = w2_scale;
+  a.b2 = (const uint16_t*)b2;
+  a.Y = (uint16_t*)Y;
+  a.M = (int)M;
+  a.K1 = (int)K1;
+  a.N1 = (int)N1;
+  a.N2 = (int)N2;
+  return hip_status(wq::launch_static_mlp2(a, (hipStream_t)stream), "wq_fp8_static_mlp2 launch");
+}
+
 size_t wq_read_stream_words(size_t bytes) { return (bytes + 16383) / 16384; }
 
 wq_status wq_read_stream(const void* p, size_t bytes, uint32_t* sink, void* stream) {

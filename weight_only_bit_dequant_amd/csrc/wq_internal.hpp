@@ -68,6 +68,23 @@ hipError_t launch_absmax(const uint16_t* X, int64_t numel, float* amax, hipStrea
 hipError_t launch_fp8_scale(const float* amax, float* scale, int64_t count, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* X, int64_t numel, const float* act_scale, uint8_t* Xq,
                                hipStream_t s);
+// Fused two-layer static-FP8 MLP
+struct Mlp2Args {
+  const uint16_t* X;                 // bf16 [M][K1]
+  const float* act_scale1;           // layer-1 activation scale (device)
+  const uint8_t* W1;                 // E4M3 [N1][K1]
+  const float* w1_scale;             // [N1]
+  const uint16_t* b1;                // bf16 [N1] or null
+  const float* act_scale2;           // layer-2 activation scale (device)
+  const uint8_t* W2;                 // E4M3 [N2][N1]
+  const float* w2_scale;             // [N2]
+  const uint16_t* b2;                // bf16 [N2] or null
+  uint16_t* Y;                       // bf16 [M][N2]
+  int M, K1, N1, N2;
+};
+size_t mlp2_smem_bytes(int64_t K1, int64_t N1, int64_t N2);
+hipError_t launch_static_mlp2(const Mlp2Args& a, hipStream_t s);
+
 // MXFP4 dynamic-activation path
 hipError_t launch_mx_quantize_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, uint8_t* Xs, hipStream_t s);
 hipError_t launch_mx_linear(const LinearArgs& a, hipStream_t s);

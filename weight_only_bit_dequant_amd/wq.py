@@ -70,11 +70,13 @@ def lib():
         L.wq_mxfp4_dynamic_workspace.restype = SZ
         L.wq_mxfp4_dynamic_linear.argtypes = [P, I64, I64, P, P, P, I64, P, P, SZ, P]
         L.wq_read_stream.argtypes = [P, SZ, P, P]
+        L.wq_fp8_static_mlp2.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, P, P, I64, P, P]
         L.wq_read_stream_words.argtypes = [SZ]
         L.wq_read_stream_words.restype = SZ
         for name in ("wq_layout", "wq_quantize", "wq_pack", "wq_dequantize", "wq_linear", "wq_absmax",
                      "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear", "wq_fp8_linear",
-                     "wq_read_stream", "wq_mx_quantize_act", "wq_mx_linear", "wq_mxfp4_dynamic_linear"):
+                     "wq_read_stream", "wq_mx_quantize_act", "wq_mx_linear", "wq_mxfp4_dynamic_linear",
+                     "wq_fp8_static_mlp2"):
             getattr(L, name).restype = I
         if L.wq_abi_version() != 1:
             raise RuntimeError("libwq ABI version mismatch")
@@ -203,6 +205,14 @@ def wq_mxfp4_dynamic_linear(X, Wq, Ws, bias, N, Y, workspace):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().wq_mxfp4_dynamic_linear(_ptr(X), M, K, _ptr(Wq), _ptr(Ws), _ptr(bias), N, _ptr(Y),
                                          _ptr(workspace), ws_bytes, _stream(X.device)), "wq_mxfp4_dynamic_linear")
+
+
+def wq_fp8_static_mlp2(X, act_scale1, W1q, w1_scale, b1, act_scale2, W2q, w2_scale, b2, Y):
+    M, K1 = X.shape
+    N1, N2 = W1q.shape[0], W2q.shape[0]
+    _check(lib().wq_fp8_static_mlp2(_ptr(X), M, K1, _ptr(act_scale1), _ptr(W1q), _ptr(w1_scale), _ptr(b1), N1,
+                                    _ptr(act_scale2), _ptr(W2q), _ptr(w2_scale), _ptr(b2), N2, _ptr(Y),
+                                    _stream(X.device)), "wq_fp8_static_mlp2")
 
 
 def wq_read_stream_words(nbytes):
