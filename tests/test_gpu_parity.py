@@ -238,6 +238,24 @@ def test_static_act_quant_and_calibration_bit_exact():
     assert np.array_equal(host(Xq2), S.quantize_act(X2, s_ref))
 
 
+@pytest.mark.parametrize("scale", [1.0, 0.0, 3.0, 0.0123, 448.0 / 3.0e4, 2.0 ** -10, 7.5e-5, 1.7e3])
+def test_static_act_quant_every_bf16(scale):
+    """Every non-NaN bf16 value (infinities, zeros, subnormals included)
+    through the static activation Q at several scales: the E4M3 codes equal
+    the oracle's bit for bit.  The quotients x / s cover the E4M3 subnormal
+    range, rounding ties and saturation.  The element count is ragged
+    (65282 = 8 * 8160 + 2)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    nan = ((bits & 0x7F80) == 0x7F80) & ((bits & 0x007F) != 0)
+    X = bits[~nan].reshape(1, -1)
+    print(f"[case] static act quant every bf16, scale {scale}", flush=True)
+    t_s = torch.tensor([scale], dtype=torch.float32, device=DEV)
+    Xq = torch.empty(X.shape, dtype=torch.uint8, device=DEV)
+    wq.wq_fp8_quantize_act(dev_bf16(X), t_s, Xq)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Xq), S.quantize_act(X, np.float32(scale)))
+
+
 def _gpu_static_layer(x_dev, act_scale, Wq, w_scale):
     return wq.static_fp8_linear(x_dev, act_scale, Wq, w_scale)
 

@@ -24,10 +24,18 @@ namespace wq {
 
 namespace {
 
-// E4M3 code of bf16 x divided by s (the static activation Q).
-__device__ __forceinline__ uint32_t q_act(float x, float s) {
-  const float q = (s > 0.f) ? x / s : x;
-  return e4m3_encode(clampf(q, -448.f, 448.f));
+// The static activation Q before rounding: clamp(x / s, +-448) (x itself when
+// s == 0); e4m3_cvt / e4m3_pack4 round it to E4M3.
+__device__ __forceinline__ float q_val(float x, float s) {
+  return clampf((s > 0.f) ? x / s : x, -448.f, 448.f);
+}
+__device__ __forceinline__ uint32_t q_act(float x, float s) { return e4m3_cvt(q_val(x, s)); }
+// eight bf16 values (four words) -> eight codes
+__device__ __forceinline__ u32x2 q_act8(u32x4 v, float s) {
+  return u32x2{e4m3_pack4(q_val(bitsf(v.x << 16), s), q_val(bitsf(v.x & 0xFFFF0000u), s), q_val(bitsf(v.y << 16), s),
+                          q_val(bitsf(v.y & 0xFFFF0000u), s)),
+               e4m3_pack4(q_val(bitsf(v.z << 16), s), q_val(bitsf(v.z & 0xFFFF0000u), s), q_val(bitsf(v.w << 16), s),
+                          q_val(bitsf(v.w & 0xFFFF0000u), s))};
 }
 
 __device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -170,12 +178,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_static_mlp2_sp(Mlp2Args a) {
 
   // ---- X -> E4M3 codes; layer-1 weight rows -> the wave's slab
   if (xr < 16) {
-    u32x2 q;
-    q.x = q_act(bitsf(xv.x << 16), s1) | (q_act(bitsf(xv.x & 0xFFFF0000u), s1) << 8) |
-          (q_act(bitsf(xv.y << 16), s1) << 16) | (q_act(bitsf(xv.y & 0xFFFF0000u), s1) << 24);
-    q.y = q_act(bitsf(xv.z << 16), s1) | (q_act(bitsf(xv.z & 0xFFFF0000u), s1) << 8) |
-          (q_act(bitsf(xv.w << 16), s1) << 16) | (q_act(bitsf(xv.w & 0xFFFF0000u), s1) << 24);
-    *reinterpret_cast<u32x2*>(Xq + xr * kSpRS1 + xk) = q;
+    *reinterpret_cast<u32x2*>(Xq + xr * kSpRS1 + xk) = q_act8(xv, s1);
   }
   store_slab(slab, w1, lane);
   __syncthreads();
@@ -282,12 +285,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_static_mlp2(Mlp2Args a) {
   for (int i = tid; i < 16 * K1 / 8; i += NTHR) {
     const int r = (i * 8) / K1, k = (i * 8) % K1;
     const u32x4 v = bload128(Xr, ((uint32_t)(m0 + r) * (uint32_t)K1 + (uint32_t)k) * 2u);  // rows past M read 0
-    u32x2 q;
-    q.x = q_act(bitsf(v.x << 16), s1) | (q_act(bitsf(v.x & 0xFFFF0000u), s1) << 8) |
-          (q_act(bitsf(v.y << 16), s1) << 16) | (q_act(bitsf(v.y & 0xFFFF0000u), s1) << 24);
-    q.y = q_act(bitsf(v.z << 16), s1) | (q_act(bitsf(v.z & 0xFFFF0000u), s1) << 8) |
-          (q_act(bitsf(v.w << 16), s1) << 16) | (q_act(bitsf(v.w & 0xFFFF0000u), s1) << 24);
-    *reinterpret_cast<u32x2*>(Xq + r * RS1 + k) = q;
+    *reinterpret_cast<u32x2*>(Xq + r * RS1 + k) = q_act8(v, s1);
   }
   __syncthreads();
 

@@ -319,14 +319,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(const uint16_t* __restri
   if (id < full) {
     u32x4 v = reinterpret_cast<const u32x4*>(X)[id];
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[2] = {0, 0};
+    float q[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float x = bitsf((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
-      float q = (s > 0.f) ? x / s : x;
-      o[i >> 2] |= e4m3_encode(clampf(q, -448.f, 448.f)) << (8 * (i & 3));
+      q[i] = clampf((s > 0.f) ? x / s : x, -448.f, 448.f);
     }
-    reinterpret_cast<u32x2*>(Xq)[id] = u32x2{o[0], o[1]};
+    reinterpret_cast<u32x2*>(Xq)[id] = u32x2{e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7])};
   } else if (id == full) {
     for (int64_t i = full * 8; i < numel; ++i) {
       float x = bf16_to_f32(X[i]);
