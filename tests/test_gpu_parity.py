@@ -352,6 +352,29 @@ def test_fp8_linear_on_prequantized_activations(M, N, K, bias):
     assert_close(Y1, S.static_linear_fp64(xq_ref, s_ref, wq_ref, ws_ref, b), f"fp8_linear M={M} N={N}")
 
 
+@pytest.mark.parametrize("M,N,K,bias", [(3000, 4160, 1040, True), (520, 6000, 208, True), (1000, 1000, 1104, False)])
+def test_fp8_tiled_ragged(M, N, K, bias):
+    """Static-FP8 GEMM in its three tiled forms (256 x 256, 128 x 128 and
+    64 x 64 tiles, chosen by the tile count) with ragged M and N tiles and a
+    partial last K step; sampled rows against the oracle."""
+    W, b, X = synth.linear_case(N, K, M, cfg=90 + K % 7)
+    b = b if bias else None
+    print(f"[case] fp8 tiled ragged M={M} N={N} K={K} bias={bias}", flush=True)
+    scale, _ = wq.calibrate_act_scale([dev_bf16(X[:64])])
+    q = wq.quantize("fp8", dev_bf16(W))
+    Xq = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    wq.wq_fp8_quantize_act(dev_bf16(X), scale, Xq)
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(1, wq.wq_fp8_linear_workspace(M, N, K)), dtype=torch.uint8, device=DEV)
+    wq.wq_fp8_linear(Xq, scale, q["codes"], q["scales"], dev_bf16(b) if b is not None else None, Y, ws)
+    torch.cuda.synchronize()
+    s_ref = S.scale_from_amax(S.absmax(X[:64]))
+    wq_ref, ws_ref = Q.quantize_fp8_row(W)
+    rows = np.unique(np.concatenate([np.arange(0, M, 37), [M - 1]]))
+    ref = S.static_linear_fp64(S.quantize_act(X[rows], s_ref), s_ref, wq_ref, ws_ref, b)
+    assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"fp8 tiled M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("nbytes", [16, 1040, 16384 + 48, 4096 * 1536])
 def test_read_stream_xor(nbytes):
     """The measurement stream reads every byte: each block's XOR equals the host's."""

@@ -393,7 +393,7 @@ hipError_t launch_gemm_tiled(int kfmt, const LinearArgs& a, const LinearPlan& p,
     case KF_FP8: return launch_tiled_f<KF_FP8>(a, p, s);
     case KF_NVFP4: return launch_tiled_f<KF_NVFP4>(a, p, s);
     case KF_MXFP4: return launch_tiled_f<KF_MXFP4>(a, p, s);
-    case KF_FP8S: return launch_tiled_f<KF_FP8S>(a, p, s);
+    case KF_FP8S: return launch_f8_gemm_tiled(a, s);
     default: return hipErrorInvalidValue;
   }
 }

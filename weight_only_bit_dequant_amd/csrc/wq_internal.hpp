@@ -88,5 +88,7 @@ hipError_t launch_static_mlp2(const Mlp2Args& a, hipStream_t s);
 // MXFP4 dynamic-activation path
 hipError_t launch_mx_quantize_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, uint8_t* Xs, hipStream_t s);
 hipError_t launch_mx_linear(const LinearArgs& a, hipStream_t s);
+// static FP8 tiled GEMM on the scaled matrix cores (E4M3 x E4M3, unit scales)
+hipError_t launch_f8_gemm_tiled(const LinearArgs& a, hipStream_t s);
 
 }  // namespace wq

@@ -30,6 +30,14 @@ __device__ __forceinline__ f32x4 mfma_mx4(u32x4 a, uint32_t sa, u32x4 b, uint32_
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
+// E4M3 x E4M3 on the same instruction (cbsz = blgp = 0): lane (g, c) supplies
+// 32 codes of row/column c, K 32g .. 32g+31 (byte j of the 32 = K 32g + j),
+// both block scales 2^0 (code 127).  A device probe confirmed the layout
+// against a host model.
+__device__ __forceinline__ f32x4 mfma_f8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 // ---------------------------------------------------------------- activation quantizer
 // One thread per 32-element block of a row: the block's max |x| sets
 // e = floor(log2 amax) - 2 (from the bf16 exponent field; zero and subnormal
@@ -161,27 +169,42 @@ __global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
 // multiples, or too long for LDS) every step loads 4 scale bytes per row;
 // those loads touch a different row per lane and were measured to dominate
 // the step time when they are used.
-template <int BM, int BN, int GT>
+template <int BM, int BN, int GT, bool F8>
 struct MxTile {
-  static constexpr int ROWB = 64;                       // packed bytes of one row per step
+  static constexpr int ROWB = F8 ? 128 : 64;            // operand bytes of one row per step
+  static constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row and step
+  static constexpr int KPC = F8 ? 16 : 32;              // K elements per chunk
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-  static constexpr int AS_BYTES = BM * 4, BS_BYTES = BN * 4;  // per-step scale planes (no PRE)
+  static constexpr int AS_BYTES = F8 ? 0 : BM * 4, BS_BYTES = F8 ? 0 : BN * 4;  // per-step scale planes (no PRE)
   static constexpr int BUF = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
   static constexpr int TILES = 2 * BUF;
-  static constexpr int NA = BM * 4 / GT, NB = BN * 4 / GT;  // 16-byte chunks per thread
-  __device__ static __forceinline__ int pos(int r, int k) { return k ^ ((r >> 1) & 3); }
+  static constexpr int NA = BM * CPR / GT, NB = BN * CPR / GT;  // 16-byte chunks per thread
+  // LDS slot of chunk k of row r.  A ds_read_b128 serves lanes 0-7 with
+  // 16-23 (8-15 with 24-31, ...) together: the 16 reads of rows c = 0..7 by
+  // lane groups g and g+1 must hit distinct 16-byte bank groups of the row
+  // window they fall in.  E2M1 rows (64 bytes, lane reads chunk g): XOR with
+  // row bits 1-2.  E4M3 rows (128 bytes, lane reads chunks 2g and 2g+1): XOR
+  // with row bits 1 and 2 as 1 and 4.  Whole-row writes are conflict-free
+  // under any XOR.
+  __device__ static __forceinline__ int pos(int r, int k) {
+    return F8 ? (k ^ (((r >> 1) & 1) | (r & 4))) : (k ^ ((r >> 1) & 3));
+  }
   // LDS for the whole-K scale rows (PRE)
   static size_t pre_bytes(int K) { return (size_t)(BM + BN) * (size_t)(K / 32); }
 };
 
 // WGN waves along N (2 x WGN wave grid, GT = 128 * WGN threads); each wave
-// owns a (BM/2) x (BN/WGN) block.
-template <int BM, int BN, int WGN, bool PRE>
+// owns a (BM/2) x (BN/WGN) block.  F8: E4M3 operands (static FP8 path): 128
+// bytes per row and step, no block scales (the MFMA takes 2^0 for both), the
+// epilogue applies act_scale * w_scale[n].
+template <int BM, int BN, int WGN, bool PRE, bool F8>
 __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
   constexpr int GT = 128 * WGN, WBN = BN / WGN;
-  using TT = MxTile<BM, BN, GT>;
+  using TT = MxTile<BM, BN, GT, F8>;
   constexpr int TM = BM / 32, TN = WBN / 16;
-  static_assert(TT::NA >= 1 && TT::NB >= 1 && TT::NA * GT == BM * 4 && TT::NB * GT == BN * 4,
+  constexpr int CPR = TT::CPR;
+  static_assert(!(PRE && F8), "E4M3 operands have no block scales");
+  static_assert(TT::NA >= 1 && TT::NB >= 1 && TT::NA * GT == BM * CPR && TT::NB * GT == BN * CPR,
                 "tile rows must split evenly over the threads");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -195,11 +218,11 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
   if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
   const int n0 = (b % gx) * BN, m0 = (b / gx) * BM;
 
-  const uint32_t rowb = (uint32_t)K / 2u, srow = (uint32_t)K / 32u;
+  const uint32_t rowb = F8 ? (uint32_t)K : (uint32_t)K / 2u, srow = (uint32_t)K / 32u;
   const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * rowb);
-  const __amdgpu_buffer_rsrc_t Xsr = make_rsrc(a.xscales, (uint32_t)M * srow);
   const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * rowb);
-  const __amdgpu_buffer_rsrc_t Wsr = make_rsrc(a.scales, (uint32_t)N * srow);
+  const __amdgpu_buffer_rsrc_t Xsr = make_rsrc(F8 ? a.X : (const void*)a.xscales, F8 ? 0u : (uint32_t)M * srow);
+  const __amdgpu_buffer_rsrc_t Wsr = make_rsrc(a.scales, F8 ? (uint32_t)N * 4u : (uint32_t)N * srow);
   const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
   const int KT = (K + 127) / 128;
   unsigned char* XS = smem + TT::TILES;    // PRE: [BM][srow] activation scale rows
@@ -215,24 +238,24 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
       *reinterpret_cast<u32x4*>(WS + 16 * q) = bload128(Wsr, (uint32_t)n0 * srow + 16u * q);
   }
 
-  // loads of one step: chunk q of this thread is row (q*256 + tid) / 4, part % 4
+  // loads of one step: chunk q of this thread is row (q*GT + tid) / CPR, part % CPR
   u32x4 xa[2][TT::NA], wb[2][TT::NB];
-  uint32_t xsb[2][4], wsb[2][4];  // raw scale bytes (no PRE)
+  uint32_t xsb[2][4], wsb[2][4];  // raw scale bytes (MX without PRE)
   auto gload = [&](int kt, int st) {
-    const uint32_t kb = (uint32_t)kt * 64u;  // byte offset of the step in a packed row
+    const uint32_t kb = (uint32_t)kt * (uint32_t)TT::ROWB;  // byte offset of the step in a row
 #pragma unroll
     for (int q = 0; q < TT::NA; ++q) {
-      const int id = q * GT + tid, row = id >> 2, part = id & 3;
-      const bool ok = kt * 128 + part * 32 < K;
+      const int id = q * GT + tid, row = id / CPR, part = id % CPR;
+      const bool ok = kt * 128 + part * TT::KPC < K;
       xa[st][q] = bload128(Xr, off_if(ok, (uint32_t)(m0 + row) * rowb + kb + 16u * part));
     }
 #pragma unroll
     for (int q = 0; q < TT::NB; ++q) {
-      const int id = q * GT + tid, row = id >> 2, part = id & 3;
-      const bool ok = kt * 128 + part * 32 < K;
+      const int id = q * GT + tid, row = id / CPR, part = id % CPR;
+      const bool ok = kt * 128 + part * TT::KPC < K;
       wb[st][q] = bload128(Wr, off_if(ok, (uint32_t)(n0 + row) * rowb + kb + 16u * part));
     }
-    if constexpr (!PRE) {
+    if constexpr (!PRE && !F8) {
       // thread t reads the step's 4 scale bytes of activation row t % BM and
       // weight row t % BN (threads past the row count repeat a row, so no
       // thread needs a branch); bytes past K read zero
@@ -249,15 +272,15 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
     unsigned char* B = A + TT::A_BYTES;
 #pragma unroll
     for (int q = 0; q < TT::NA; ++q) {
-      const int id = q * GT + tid, row = id >> 2, part = id & 3;
+      const int id = q * GT + tid, row = id / CPR, part = id % CPR;
       *reinterpret_cast<u32x4*>(A + row * TT::ROWB + TT::pos(row, part) * 16) = xa[st][q];
     }
 #pragma unroll
     for (int q = 0; q < TT::NB; ++q) {
-      const int id = q * GT + tid, row = id >> 2, part = id & 3;
+      const int id = q * GT + tid, row = id / CPR, part = id % CPR;
       *reinterpret_cast<u32x4*>(B + row * TT::ROWB + TT::pos(row, part) * 16) = wb[st][q];
     }
-    if constexpr (!PRE) {
+    if constexpr (!PRE && !F8) {
       // scale planes [block j][row]: byte stores straight from the loaded
       // registers, BM apart, so the compiler does not merge them into words
       // (which would make it wait for all four loads); repeated rows store
@@ -272,9 +295,14 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
     }
   };
 
-  uint32_t bias_bits[TN];
+  uint32_t bias_bits[TN], cs_bits[TN];
 #pragma unroll
-  for (int t = 0; t < TN; ++t) bias_bits[t] = bload16(Br, (uint32_t)(n0 + wn * WBN + 16 * t + c) * 2u);
+  for (int t = 0; t < TN; ++t) {
+    const uint32_t n = (uint32_t)(n0 + wn * WBN + 16 * t + c);
+    bias_bits[t] = bload16(Br, n * 2u);
+    cs_bits[t] = F8 ? bload32(Wsr, n * 4u) : 0x3F800000u;
+  }
+  const float s1 = F8 ? a.act_scale[0] : 1.0f;
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -285,27 +313,51 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
   auto compute = [&](int buf, int kt) {
     const unsigned char* A = smem + buf * TT::BUF;
     const unsigned char* B = A + TT::A_BYTES;
-    const unsigned char* AS = B + TT::B_BYTES;
-    const unsigned char* BS = AS + TT::AS_BYTES;
-    u32x4 af[TM], bf[TN];
-    uint32_t as[TM], bs[TN];
+    if constexpr (F8) {
+      // lane (g, c): row/column c, K 32g .. 32g+31 of the step = chunks 2g and
+      // 2g+1 of the row
+      i32x8 af[TM], bf[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = wm * (BM / 2) + 16 * i + c;
-      af[i] = *reinterpret_cast<const u32x4*>(A + r * TT::ROWB + TT::pos(r, g) * 16);
-      // blocks past K have zero codes; their scale is taken as 2^0
-      as[i] = PRE ? ((4 * kt + g < (int)srow) ? XS[r * srow + min(4 * kt + g, (int)srow - 1)] : 127u) : AS[g * BM + r];
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + 16 * i + c;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(A + r * TT::ROWB + TT::pos(r, 2 * g) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(A + r * TT::ROWB + TT::pos(r, 2 * g + 1) * 16);
+        af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * WBN + 16 * t + c;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(B + r * TT::ROWB + TT::pos(r, 2 * g) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(B + r * TT::ROWB + TT::pos(r, 2 * g + 1) * 16);
+        bf[t] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[i][t] = mfma_f8(af[i], bf[t], acc[i][t]);
+    } else {
+      const unsigned char* AS = B + TT::B_BYTES;
+      const unsigned char* BS = AS + TT::AS_BYTES;
+      u32x4 af[TM], bf[TN];
+      uint32_t as[TM], bs[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + 16 * i + c;
+        af[i] = *reinterpret_cast<const u32x4*>(A + r * TT::ROWB + TT::pos(r, g) * 16);
+        // blocks past K have zero codes; their scale is taken as 2^0
+        as[i] = PRE ? ((4 * kt + g < (int)srow) ? XS[r * srow + min(4 * kt + g, (int)srow - 1)] : 127u) : AS[g * BM + r];
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * WBN + 16 * t + c;
+        bf[t] = *reinterpret_cast<const u32x4*>(B + r * TT::ROWB + TT::pos(r, g) * 16);
+        bs[t] = PRE ? ((4 * kt + g < (int)srow) ? WS[r * srow + min(4 * kt + g, (int)srow - 1)] : 127u) : BS[g * BN + r];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[i][t] = mfma_mx4(af[i], as[i], bf[t], bs[t], acc[i][t]);
     }
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const int r = wn * WBN + 16 * t + c;
-      bf[t] = *reinterpret_cast<const u32x4*>(B + r * TT::ROWB + TT::pos(r, g) * 16);
-      bs[t] = PRE ? ((4 * kt + g < (int)srow) ? WS[r * srow + min(4 * kt + g, (int)srow - 1)] : 127u) : BS[g * BN + r];
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int t = 0; t < TN; ++t) acc[i][t] = mfma_mx4(af[i], as[i], bf[t], bs[t], acc[i][t]);
   };
 
   // two register stages, two LDS buffers; the step count is even so both
@@ -331,27 +383,148 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int n = n0 + wn * WBN + 16 * t + c;
-    const float bias = bitsf(bias_bits[t] << 16);
+    const float bias = bitsf(bias_bits[t] << 16), cs = bitsf(cs_bits[t]);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
-        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][t][r] + bias);
+        const float y = F8 ? (acc[i][t][r] * s1) * cs : acc[i][t][r];
+        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- static FP8, 256 x 256 tiles
+// For large M x N: a workgroup of 8 waves (2 x 4 wave grid, 128 x 64 outputs
+// per wave) owns a 256 x 256 tile; K advances 128 per step on the E4M3 scaled
+// MFMA.  Operand rows go from memory straight into LDS (buffer_load_dwordx4
+// ... lds writes lane i's 16 bytes at the wave's LDS base + 16 i): one load
+// moves 8 whole 128-byte rows, and the bank swizzle is applied by choosing
+// which 16-byte chunk of its row each lane reads.  Two LDS stages of 64 KiB.
+// Per step a wave waits for its loads and meets the others at the one barrier
+// of the step, issues the loads of the next step into the other stage, then
+// reads its operands and runs its 32 MFMAs.
+constexpr int kF8T = 256;                 // tile rows and columns
+constexpr int kF8Stage = 2 * kF8T * 128;  // one LDS stage: A then B, 128 codes per row
+constexpr int kF8Smem = 2 * kF8Stage;
+
+// LDS slot of 16-byte chunk k (0..7) of tile row r.  An operand read has lane
+// (g, c) take chunks 2g and 2g+1 of row c; a ds_read_b128 serves lanes 0-7
+// with 16-23 (and 8-15 with 24-31, ...) together, so rows 0..7 with chunks
+// {0, 2} (or {1, 3}, {4, 6}, {5, 7}) must land on 16 distinct 16-byte bank
+// groups: rows of one parity share a 256-byte bank window, and within it the
+// XOR with row bits 1 and 2 (as 1 and 4) spreads the four rows' two chunks
+// over all eight slots.
+__device__ __forceinline__ int f8pos(int r, int k) { return k ^ (((r >> 1) & 1) | (r & 4)); }
+
+__global__ __launch_bounds__(512) void k_f8_gemm256(LinearArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int TM = 8, TN = 4;  // 16 x 16 tiles per wave
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int M = a.M, N = a.N, K = a.K;
+
+  // XCD-aware tile order (see the bf16 tiled kernel)
+  const int gx = gridDim.x, G = gx * gridDim.y;
+  int b = blockIdx.y * gx + blockIdx.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int n0 = (b % gx) * kF8T, m0 = (b / gx) * kF8T;
+
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t Sr = make_rsrc(a.scales, (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  const int KT = (K + 127) / 128;
+
+  // waves 0-3 load activation rows 64w .. 64w+63, waves 4-7 weight rows
+  // 64(w-4) ..; load j covers rows +8j .. +8j+7, lane L fills LDS slot L % 8 of
+  // row L / 8 with the chunk stored there (the slot map is its own inverse);
+  // chunks past K and rows past M / N read zero
+  const bool loadA = wave < 4;
+  const __amdgpu_buffer_rsrc_t Lr = loadA ? Xr : Wr;
+  const int lrow0 = 64 * (wave & 3);
+  const uint32_t lbase = (uint32_t)((loadA ? m0 : n0) + lrow0);
+  auto issue = [&](int kt, int st) {
+    unsigned char* dst0 = smem + st * kF8Stage + (loadA ? 0 : kF8T * 128) + lrow0 * 128;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = lrow0 + 8 * j + (lane >> 3);
+      const int kc = f8pos(r, lane & 7);
+      const bool ok = kt * 128 + 16 * kc < K;
+      const uint32_t off =
+          off_if(ok, (lbase + 8u * j + (uint32_t)(lane >> 3)) * (uint32_t)K + (uint32_t)kt * 128u + 16u * kc);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Lr, (__attribute__((address_space(3))) void*)(dst0 + j * 1024), 16, off, 0,
+                                               0, 0);
+    }
+  };
+
+  uint32_t bias_bits[TN], cs_bits[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const uint32_t n = (uint32_t)(n0 + wn * 64 + 16 * t + c);
+    bias_bits[t] = bload16(Br, n * 2u);
+    cs_bits[t] = bload32(Sr, n * 4u);
+  }
+  const float s1 = a.act_scale[0];
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // lane (g, c): row/column c, K 32g .. 32g+31 of the step = chunks 2g, 2g+1
+  auto operand = [&](const unsigned char* T, int r) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(T + r * 128 + f8pos(r, 2 * g) * 16);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(T + r * 128 + f8pos(r, 2 * g + 1) * 16);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  issue(0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of step kt are in LDS
+    __syncthreads();                     // ... and every wave's; stage (kt+1)&1 is no longer read
+    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
+    const unsigned char* A = smem + (kt & 1) * kF8Stage;
+    const unsigned char* B = A + kF8T * 128;
+    i32x8 bf[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) bf[t] = operand(B, wn * 64 + 16 * t + c);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const i32x8 af = operand(A, wm * 128 + 16 * i + c);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) acc[i][t] = mfma_f8(af, bf[t], acc[i][t]);
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int n = n0 + wn * 64 + 16 * t + c;
+    const float bias = bitsf(bias_bits[t] << 16), cs = bitsf(cs_bits[t]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 128 + 16 * i + 4 * g + r;
+        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16((acc[i][t][r] * s1) * cs + bias);
       }
   }
 }
 
 template <int BM, int BN, int WGN = 2>
 hipError_t launch_mx_tile(const LinearArgs& a, hipStream_t s) {
-  using TT = MxTile<BM, BN, 128 * WGN>;
+  using TT = MxTile<BM, BN, 128 * WGN, false>;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
   const size_t pre = TT::pre_bytes(a.K);
   constexpr int limit = 128 * 1024;
   if ((a.K / 32) % 16 == 0 && TT::TILES + pre <= (size_t)limit) {
     static std::atomic<int> done{0};
     const int sm = (int)(TT::TILES + pre);
-    auto k = k_mx_gemm_tiled<BM, BN, WGN, true>;
+    auto k = k_mx_gemm_tiled<BM, BN, WGN, true, false>;
     if (sm > 65536 && !done.load(std::memory_order_acquire)) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                          limit);
@@ -361,11 +534,22 @@ hipError_t launch_mx_tile(const LinearArgs& a, hipStream_t s) {
     k<<<grid, 128 * WGN, sm, s>>>(a);
   } else {
     static std::atomic<int> done{0};
-    auto k = k_mx_gemm_tiled<BM, BN, WGN, false>;
+    auto k = k_mx_gemm_tiled<BM, BN, WGN, false, false>;
     hipError_t e = allow_smem(k, TT::TILES, done);
     if (e != hipSuccess) return e;
     k<<<grid, 128 * WGN, TT::TILES, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGN = 2>
+hipError_t launch_f8_tile(const LinearArgs& a, hipStream_t s) {
+  using TT = MxTile<BM, BN, 128 * WGN, true>;
+  static std::atomic<int> done{0};
+  auto k = k_mx_gemm_tiled<BM, BN, WGN, false, true>;
+  hipError_t e = allow_smem(k, TT::TILES, done);
+  if (e != hipSuccess) return e;
+  k<<<dim3((a.N + BN - 1) / BN, (a.M + BM - 1) / BM), 128 * WGN, TT::TILES, s>>>(a);
   return hipGetLastError();
 }
 
@@ -375,6 +559,20 @@ hipError_t launch_mx_quantize_act(const uint16_t* X, int64_t M, int64_t K, uint8
   const uint32_t nblk = (uint32_t)(M * (K / 32));
   k_mx_quant_act<<<(nblk + 255) / 256, 256, 0, s>>>(X, nblk, Xq, Xs);
   return hipGetLastError();
+}
+
+hipError_t launch_f8_gemm_tiled(const LinearArgs& a, hipStream_t s) {
+  // the largest tiles that still give most CUs a workgroup
+  const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if (t256 >= 192) {
+    static std::atomic<int> done{0};
+    hipError_t e = allow_smem(k_f8_gemm256, kF8Smem, done);
+    if (e != hipSuccess) return e;
+    k_f8_gemm256<<<dim3((a.N + kF8T - 1) / kF8T, (a.M + kF8T - 1) / kF8T), 512, kF8Smem, s>>>(a);
+    return hipGetLastError();
+  }
+  const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  return t128 >= 192 ? launch_f8_tile<128, 128>(a, s) : launch_f8_tile<64, 64>(a, s);
 }
 
 hipError_t launch_mx_linear(const LinearArgs& a, hipStream_t s) {
