@@ -248,6 +248,7 @@ wq_status wq_fp8_quantize_act(const void* X, int64_t M, int64_t K, const float* 
   if (M < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
   if (M > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
   if (M == 0 || K == 0) return ok();
+  if (M * K >= ((int64_t)1 << 43)) return fail(WQ_EUNSUPPORTED, "wq_fp8_quantize_act: 2^43 elements or more");
   if (!X || !Xq || !act_scale) return fail(WQ_EINVAL, "wq_fp8_quantize_act: null pointer");
   if (!aligned16(X) || !aligned16(Xq)) return fail(WQ_EALIGN, "X and Xq must be 16-byte aligned");
   return hip_status(wq::launch_quantize_act((const uint16_t*)X, M * K, act_scale, (uint8_t*)Xq,

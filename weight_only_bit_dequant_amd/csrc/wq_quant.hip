@@ -309,28 +309,47 @@ __global__ void k_fp8_scale(const float* __restrict__ amax, float* __restrict__ 
 }
 
 // "TorchAO Static FP8 Quantization (Linear)": x -> E4M3(clamp(x / act_scale, +-448)).
-// One thread per 8 elements; the tail (numel % 8) is handled element-wise.
+// A thread converts four 8-element chunks (chunk c = block * 1024 + q * 256 +
+// thread, q = 0..3), all four loads in flight before the first use; the
+// element tail (numel % 8) goes to the thread whose chunk index equals the
+// chunk count.
+constexpr int kQActChunks = 4;
+__device__ __forceinline__ u32x2 quant8(u32x4 v, float s) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float x = bitsf((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+    q[i] = clampf((s > 0.f) ? x / s : x, -448.f, 448.f);
+  }
+  return u32x2{e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7])};
+}
+
 __global__ __launch_bounds__(kThreads) void k_quant_act(const uint16_t* __restrict__ X, int64_t numel,
                                                         const float* __restrict__ act_scale,
                                                         uint8_t* __restrict__ Xq) {
-  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * (kThreads * kQActChunks) + threadIdx.x;
   const float s = act_scale[0];
   const int64_t full = numel / 8;
-  if (id < full) {
-    u32x4 v = reinterpret_cast<const u32x4*>(X)[id];
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float q[8];
+  const u32x4* X16 = reinterpret_cast<const u32x4*>(X);
+  u32x2* Q8 = reinterpret_cast<u32x2*>(Xq);
+  if (c0 + (kQActChunks - 1) * kThreads < full) {
+    u32x4 v[kQActChunks];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x = bitsf((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
-      q[i] = clampf((s > 0.f) ? x / s : x, -448.f, 448.f);
-    }
-    reinterpret_cast<u32x2*>(Xq)[id] = u32x2{e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7])};
-  } else if (id == full) {
-    for (int64_t i = full * 8; i < numel; ++i) {
-      float x = bf16_to_f32(X[i]);
-      float q = (s > 0.f) ? x / s : x;
-      Xq[i] = (uint8_t)e4m3_encode(clampf(q, -448.f, 448.f));
+    for (int q = 0; q < kQActChunks; ++q) v[q] = X16[c0 + q * kThreads];
+#pragma unroll
+    for (int q = 0; q < kQActChunks; ++q) Q8[c0 + q * kThreads] = quant8(v[q], s);
+    return;
+  }
+  for (int q = 0; q < kQActChunks; ++q) {
+    const int64_t c = c0 + q * kThreads;
+    if (c < full) {
+      Q8[c] = quant8(X16[c], s);
+    } else if (c == full) {
+      for (int64_t i = full * 8; i < numel; ++i) {
+        const float x = bf16_to_f32(X[i]);
+        Xq[i] = (uint8_t)e4m3_encode(clampf((s > 0.f) ? x / s : x, -448.f, 448.f));
+      }
     }
   }
 }
@@ -416,7 +435,7 @@ hipError_t launch_fp8_scale(const float* amax, float* scale, int64_t count, hipS
 
 hipError_t launch_quantize_act(const uint16_t* X, int64_t numel, const float* act_scale, uint8_t* Xq,
                                hipStream_t s) {
-  k_quant_act<<<grid_for(numel / 8 + 1), kThreads, 0, s>>>(X, numel, act_scale, Xq);
+  k_quant_act<<<grid_for(numel / 8 + 1, kThreads * kQActChunks), kThreads, 0, s>>>(X, numel, act_scale, Xq);
   return hipGetLastError();
 }
 
