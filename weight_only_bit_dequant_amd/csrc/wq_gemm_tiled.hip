@@ -6,15 +6,16 @@
 //  * every thread loads its share of the activation tile (contiguous 16-byte
 //    loads) and of the packed weight tile for the NEXT step, so global
 //    latency overlaps the current step's matrix-core work;
-//  * the weight chunk is decoded once per workgroup into bf16 (E4M3 for the
-//    static path) and written to LDS next to the activation tile (double
+//  * the weight chunk is decoded once per workgroup into bf16 and written to
+//    LDS next to the activation tile (double
 //    buffered; the 16-byte chunks of each row are XOR-swizzled with row bits
 //    so that operand reads and tile writes are free of bank conflicts);
 //  * each wave reads 16x32 operand fragments from LDS and issues
-//    v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x32_fp8_fp8 for static FP8).
+//    v_mfma_f32_16x16x32_bf16.
 // Decode: FP8 weights, NVFP4 (E2M1 x E4M3 block scale) and MXFP4 (E2M1 x
-// 2^e) are exact in bf16; the FP8 row scale, the NVFP4 global scale and the
-// static activation x weight scales go to the epilogue.  INT4 is decoded as
+// 2^e) are exact in bf16; the FP8 row scale and the NVFP4 global scale go to
+// the epilogue.  (The static FP8 path, E4M3 x E4M3, runs on the scaled
+// matrix cores in wq_mx.hip.)  INT4 is decoded as
 // bf16(code * s), the dequantized weight of the two-kernel form (at most one
 // bf16 rounding per weight).  Workgroups are mapped to tiles so that the
 // tiles resident on one XCD share activation rows in that XCD's L2.
@@ -36,24 +37,19 @@ constexpr int tile_stages() {
 
 template <int F>
 struct TileFmt {
-  static constexpr bool ACT8 = (F == KF_FP8S);
-  static constexpr int XB = ACT8 ? 1 : 2;  // bytes per activation element in LDS
-  static constexpr int OB = ACT8 ? 1 : 2;  // bytes per weight operand element in LDS
+  static constexpr int XB = 2;  // bytes per activation element in LDS (bf16)
+  static constexpr int OB = 2;  // bytes per weight operand element in LDS (bf16)
   // packed weight bytes per column per step
-  static constexpr int WSTEP = (F == KF_BF16) ? 128 : ((F == KF_FP8 || F == KF_FP8S) ? 64 : 32);
+  static constexpr int WSTEP = (F == KF_BF16) ? 128 : (F == KF_FP8 ? 64 : 32);
   static constexpr int ARS = kBK * XB;  // LDS row strides (bytes)
   static constexpr int BRS = kBK * OB;
   static_assert(ARS == BRS, "activation and weight rows share one swizzle");
-  // Position of 16-byte chunk k in LDS row r.  Rows of 8 chunks (bf16) XOR
-  // the chunk index with r & 7, rows of 4 chunks (E4M3) with (r >> 1) & 3:
-  // with these, a quarter-wave reading one chunk from each of 16 rows, and a
-  // wave writing whole rows, hit every LDS bank once (measured with the
-  // SQ_LDS_BANK_CONFLICT counter on gfx950; padding rows by 16 bytes instead
-  // doubles the read cycles).
-  __device__ static __forceinline__ int pos(int r, int k) {
-    if constexpr (ARS == 128) return k ^ (r & 7);
-    else return k ^ ((r >> 1) & 3);
-  }
+  // Position of 16-byte chunk k in LDS row r (rows of 8 chunks): the chunk
+  // index XOR r & 7.  With it, the operand reads (lane (g, c) takes chunk
+  // 4kk + g of row c) and a wave writing whole rows hit every LDS bank once
+  // (measured with the SQ_LDS_BANK_CONFLICT counter on gfx950; padding rows by
+  // 16 bytes instead doubles the read cycles).
+  __device__ static __forceinline__ int pos(int r, int k) { return k ^ (r & 7); }
 };
 
 template <int F, int BM, int BN>
@@ -98,7 +94,7 @@ __device__ __forceinline__ void decode_store(unsigned char* row, int r, int k0, 
   } else if constexpr (F == KF_FP8) {
     *at(0) = dec_fp8(w[0], w[1]);
     *at(1) = dec_fp8(w[2], w[3]);
-  } else {  // BF16 weights and E4M3 weights of the static path are stored as they are
+  } else {  // BF16 weights are stored as they are
     *reinterpret_cast<u32x4*>(at(0)) = w;
   }
 }
@@ -147,7 +143,7 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
   const int n0 = (b % gx) * BN, m0 = (b / gx) * BM;
 
-  const uint32_t wrow = (F == KF_BF16) ? 2u * (uint32_t)K : ((F == KF_FP8 || F == KF_FP8S) ? (uint32_t)K : (uint32_t)K / 2u);
+  const uint32_t wrow = (F == KF_BF16) ? 2u * (uint32_t)K : ((F == KF_FP8) ? (uint32_t)K : (uint32_t)K / 2u);
   const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * wrow);
   const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * (uint32_t)K * (uint32_t)TF::XB);
   uint32_t sbytes = 0;
@@ -155,7 +151,7 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   else if constexpr (F == KF_INT4A) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 4u;
   else if constexpr (F == KF_NVFP4) sbytes = (uint32_t)N * (uint32_t)(K / 16);
   else if constexpr (F == KF_MXFP4) sbytes = (uint32_t)N * (uint32_t)(K / 32);
-  else if constexpr (F == KF_FP8 || F == KF_FP8S) sbytes = (uint32_t)N * 4u;
+  else if constexpr (F == KF_FP8) sbytes = (uint32_t)N * 4u;
   const __amdgpu_buffer_rsrc_t Sr = make_rsrc(a.scales ? a.scales : a.W, a.scales ? sbytes : 0u);
   const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
 
@@ -186,10 +182,10 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
       const int col = id / LB, part = id % LB;
       const uint32_t n = (uint32_t)(n0 + col);
       // K elements per 16-byte chunk: 4-bit 32, FP8 16, BF16 8; k0 is the chunk's first K
-      const int kpc = (F == KF_BF16) ? 8 : ((F == KF_FP8 || F == KF_FP8S) ? 16 : 32);
+      const int kpc = (F == KF_BF16) ? 8 : ((F == KF_FP8) ? 16 : 32);
       const int k0 = kbeg + kt * kBK + part * kpc;
       const bool ok = k0 < kend;
-      const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : ((F == KF_FP8 || F == KF_FP8S) ? (uint32_t)k0 : (uint32_t)k0 / 2u);
+      const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : ((F == KF_FP8) ? (uint32_t)k0 : (uint32_t)k0 / 2u);
       wb[q] = bload128(Wr, off_if(ok, n * wrow + byte0));
       if constexpr (F == KF_INT4) sb[q] = bload16(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u));
       else if constexpr (F == KF_INT4A) sb[q] = bload32(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 4u));
@@ -220,7 +216,7 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   for (int t = 0; t < TN; ++t) {
     const uint32_t n = (uint32_t)(n0 + wn * WBN + 16 * t + c);
     bias_bits[t] = bload16(Br, n * 2u);
-    cs_bits[t] = (F == KF_FP8 || F == KF_FP8S) ? bload32(Sr, n * 4u) : 0x3F800000u;
+    cs_bits[t] = (F == KF_FP8) ? bload32(Sr, n * 4u) : 0x3F800000u;
   }
 
   f32x4 acc[TM][TN];
@@ -232,48 +228,24 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   auto compute = [&](int buf) {
     const unsigned char* A = As + buf * BM * TF::ARS;
     const unsigned char* B = Bs + buf * BN * TF::BRS;
-    if constexpr (TF::ACT8) {
-      // E4M3: lane (g, c) reads the 16-byte chunk g of its rows, i.e. K
-      // 16g .. 16g+15 of the step, and feeds its two halves to the two MFMAs
-      // (K 16g + 8kk .. +7 in MFMA kk; the same K order on both operands)
-      u32x4 af[TM], bf[TN];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 32; ++kk) {
+      // lane (g, c): K 32kk + 8g .. +7 of the step = 16-byte chunk 4kk + g
+      bf16x8 af[TM], bf[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * (BM / 2) + 16 * i + c;
-        af[i] = *reinterpret_cast<const u32x4*>(A + r * TF::ARS + TF::pos(r, g) * 16);
+        af[i] = *reinterpret_cast<const bf16x8*>(A + r * TF::ARS + TF::pos(r, 4 * kk + g) * 16);
       }
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         const int r = wn * WBN + 16 * t + c;
-        bf[t] = *reinterpret_cast<const u32x4*>(B + r * TF::BRS + TF::pos(r, g) * 16);
+        bf[t] = *reinterpret_cast<const bf16x8*>(B + r * TF::BRS + TF::pos(r, 4 * kk + g) * 16);
       }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int t = 0; t < TN; ++t)
-            acc[i][t] = mfma_fp8(af[i][2 * kk], af[i][2 * kk + 1], bf[t][2 * kk], bf[t][2 * kk + 1], acc[i][t]);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < kBK / 32; ++kk) {
-        // lane (g, c): K 32kk + 8g .. +7 of the step = 16-byte chunk 4kk + g
-        bf16x8 af[TM], bf[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int r = wm * (BM / 2) + 16 * i + c;
-          af[i] = *reinterpret_cast<const bf16x8*>(A + r * TF::ARS + TF::pos(r, 4 * kk + g) * 16);
-        }
-#pragma unroll
-        for (int t = 0; t < TN; ++t) {
-          const int r = wn * WBN + 16 * t + c;
-          bf[t] = *reinterpret_cast<const bf16x8*>(B + r * TF::BRS + TF::pos(r, 4 * kk + g) * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int t = 0; t < TN; ++t) acc[i][t] = mfma_bf16(af[i], bf[t], acc[i][t]);
-      }
+        for (int t = 0; t < TN; ++t) acc[i][t] = mfma_bf16(af[i], bf[t], acc[i][t]);
     }
   };
 
@@ -336,7 +308,6 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   // operands were fetched before the main loop
   float s1 = 1.0f;
   if constexpr (F == KF_NVFP4) s1 = a.gscale[0];
-  if constexpr (F == KF_FP8S) s1 = a.act_scale[0];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int n = n0 + wn * WBN + 16 * t + c;
@@ -348,8 +319,7 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
         float y;
-        if constexpr (F == KF_FP8S) y = (acc[i][t][r] * s1) * cs;
-        else if constexpr (F == KF_FP8) y = acc[i][t][r] * cs;
+        if constexpr (F == KF_FP8) y = acc[i][t][r] * cs;
         else y = acc[i][t][r] * s1;
         if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
       }
@@ -374,7 +344,7 @@ template <int F>
 hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   // 128 x 128 tiles are planned only when there are enough of them (no K
   // groups); the other shapes run with one or two K groups
-  if constexpr (F == KF_MXFP4 || F == KF_FP8 || F == KF_FP8S) {
+  if constexpr (F == KF_MXFP4 || F == KF_FP8) {
     if (p.bm == 256) return launch_tile<F, 256, 256, 1, 4>(a, s);
   }
   if (p.bm == 128 && p.bn == 128) return launch_tile<F, 128, 128, 1>(a, s);

@@ -433,15 +433,16 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
   LinearPlan p{};
   if (M > 64) {
     // MFMA-bound: LDS-tiled GEMM; the largest tile that still gives about
-    // 192 workgroups
+    // 192 workgroups.  (The static FP8 GEMM's tiled kernels choose their own
+    // tiles by the same rule; for it only cfg and the zero workspace matter.)
     p.cfg = kCfgTiled;
     p.S = 1;
     p.bm = 64;
     p.bn = 64;
     // 256 x 256 tiles (8 waves) only where the decode is light enough to fit
-    // the registers of two waves per SIMD without spilling (MXFP4, FP8, E4M3
-    // x E4M3); the INT4 and NVFP4 decodes spill there and run 128 x 128.
-    const bool big_ok = kfmt == KF_MXFP4 || kfmt == KF_FP8 || kfmt == KF_FP8S;
+    // the registers of two waves per SIMD without spilling (MXFP4, FP8); the
+    // INT4 and NVFP4 decodes spill there and run 128 x 128.
+    const bool big_ok = kfmt == KF_MXFP4 || kfmt == KF_FP8;
     const int cand[4][2] = {{256, 256}, {128, 128}, {128, 64}, {64, 128}};
     for (const auto& cb : cand) {
       if (cb[0] == 256 && !big_ok) continue;

@@ -9,15 +9,16 @@
 // waves owns 16 rows and keeps them on chip end to end:
 //   1. X rows -> E4M3 codes with act_scale1 (fp32 division, clamp, nearest
 //      even) into LDS;
-//   2. layer 1: each wave takes two 16-column tiles of the hidden layer per
-//      pass (all their weight loads in flight together),
-//      v_mfma_f32_16x16x32_fp8_fp8 over K1 with the E4M3 weight rows streamed
-//      from memory; epilogue h = bf16(acc * act_scale1 * w1_scale[n] (+ b1)),
-//      then the layer-2 Q (h / act_scale2 -> E4M3) straight into LDS;
+//   2. layer 1 on v_mfma_f32_16x16x32_fp8_fp8 over K1; epilogue
+//      h = bf16(acc * act_scale1 * w1_scale[n] (+ b1)), then the layer-2 Q
+//      (h / act_scale2 -> E4M3) straight into LDS;
 //   3. layer 2 the same way over the hidden codes; y = bf16(acc * act_scale2 *
 //      w2_scale[n] (+ b2)) is the only store.
-// Every step uses the unfused path's arithmetic, so results differ from it
-// only through the order of fp32 accumulation.
+// Two forms: a single-pass kernel for models one workgroup covers in one pass
+// (the page's model), with every global load issued up front, and a looped
+// kernel for larger layers (up to the LDS limit).  Every step uses the
+// unfused path's arithmetic, so results differ from it only through the order
+// of fp32 accumulation.
 #include "wq_kernel_common.hpp"
 
 namespace wq {

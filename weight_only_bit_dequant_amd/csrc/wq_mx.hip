@@ -1,5 +1,8 @@
-// MXFP4 dynamic-activation x MXFP4-weight Linear on the gfx950 scaled matrix
-// cores.
+// GEMMs on the gfx950 scaled matrix cores (v_mfma_scale_f32_*_f8f6f4):
+//  * the MXFP4 dynamic-activation x MXFP4-weight Linear (below);
+//  * the static-FP8 (E4M3 x E4M3) GEMM for larger M, with unit block scales
+//    ("TorchAO Static FP8 Quantization (Linear)": after Q/DQ fusion the GEMM
+//    runs in FP8), further down.
 //
 // "TorchAO MXFP4 Dynamic Activation + MX Weight (Linear)", intro: the weights
 // are MXFP4 (E2M1 codes, E8M0 scale per 32 K); the activations are quantized
