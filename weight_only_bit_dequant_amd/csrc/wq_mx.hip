@@ -399,15 +399,16 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------- static FP8, 256 x 256 tiles
-// For large M x N: a workgroup of 8 waves (2 x 4 wave grid, 128 x 64 outputs
-// per wave) owns a 256 x 256 tile; K advances 128 per step on the E4M3 scaled
-// MFMA.  Operand rows go from memory straight into LDS (buffer_load_dwordx4
-// ... lds writes lane i's 16 bytes at the wave's LDS base + 16 i): one load
-// moves 8 whole 128-byte rows, and the bank swizzle is applied by choosing
-// which 16-byte chunk of its row each lane reads.  Two LDS stages of 64 KiB.
+// For large M x N: a workgroup of 16 waves (4 x 4 wave grid, 64 x 64 outputs
+// per wave; 16 waves measured 7 % faster than 8 waves of 128 x 64) owns a
+// 256 x 256 tile; K advances 128 per step on the E4M3 scaled MFMA.  Operand
+// rows go from memory straight into LDS (buffer_load_dwordx4 ... lds writes
+// lane i's 16 bytes at the wave's LDS base + 16 i): one load moves 8 whole
+// 128-byte rows, and the bank swizzle is applied by choosing which 16-byte
+// chunk of its row each lane reads.  Two LDS stages of 64 KiB.
 // Per step a wave waits for its loads and meets the others at the one barrier
 // of the step, issues the loads of the next step into the other stage, then
-// reads its operands and runs its 32 MFMAs.
+// reads its operands and runs its 16 MFMAs.
 constexpr int kF8T = 256;                 // tile rows and columns
 constexpr int kF8Stage = 2 * kF8T * 128;  // one LDS stage: A then B, 128 codes per row
 constexpr int kF8Smem = 2 * kF8Stage;
@@ -421,13 +422,19 @@ constexpr int kF8Smem = 2 * kF8Stage;
 // over all eight slots.
 __device__ __forceinline__ int f8pos(int r, int k) { return k ^ (((r >> 1) & 1) | (r & 4)); }
 
-__global__ __launch_bounds__(512) void k_f8_gemm256(LinearArgs a) {
+constexpr int kF8Waves = 16;
+
+__global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int TM = 8, TN = 4;  // 16 x 16 tiles per wave
+  // 16 x 16 tiles per wave (WBM x 64 outputs); the first half of the waves
+  // loads activation rows, the second half weight rows, LROWS rows each, in
+  // LJ loads of 8 rows per step
+  constexpr int NW = kF8Waves, WBM = 1024 / NW, TM = WBM / 16, TN = 4;
+  constexpr int HALF = NW / 2, LROWS = kF8T / HALF, LJ = LROWS / 8;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 2, wn = wave & 3;  // NW/4 x 4 wave grid
   const int M = a.M, N = a.N, K = a.K;
 
   // XCD-aware tile order (see the bf16 tiled kernel)
@@ -442,18 +449,18 @@ __global__ __launch_bounds__(512) void k_f8_gemm256(LinearArgs a) {
   const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
   const int KT = (K + 127) / 128;
 
-  // waves 0-3 load activation rows 64w .. 64w+63, waves 4-7 weight rows
-  // 64(w-4) ..; load j covers rows +8j .. +8j+7, lane L fills LDS slot L % 8 of
-  // row L / 8 with the chunk stored there (the slot map is its own inverse);
-  // chunks past K and rows past M / N read zero
-  const bool loadA = wave < 4;
+  // wave w < HALF loads activation rows LROWS*w .., wave w >= HALF weight rows
+  // LROWS*(w-HALF) ..; load j covers rows +8j .. +8j+7, lane L fills LDS slot
+  // L % 8 of row L / 8 with the chunk stored there (the slot map is its own
+  // inverse); chunks past K and rows past M / N read zero
+  const bool loadA = wave < HALF;
   const __amdgpu_buffer_rsrc_t Lr = loadA ? Xr : Wr;
-  const int lrow0 = 64 * (wave & 3);
+  const int lrow0 = LROWS * (wave % HALF);
   const uint32_t lbase = (uint32_t)((loadA ? m0 : n0) + lrow0);
   auto issue = [&](int kt, int st) {
     unsigned char* dst0 = smem + st * kF8Stage + (loadA ? 0 : kF8T * 128) + lrow0 * 128;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < LJ; ++j) {
       const int r = lrow0 + 8 * j + (lane >> 3);
       const int kc = f8pos(r, lane & 7);
       const bool ok = kt * 128 + 16 * kc < K;
@@ -498,7 +505,7 @@ __global__ __launch_bounds__(512) void k_f8_gemm256(LinearArgs a) {
     for (int t = 0; t < TN; ++t) bf[t] = operand(B, wn * 64 + 16 * t + c);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const i32x8 af = operand(A, wm * 128 + 16 * i + c);
+      const i32x8 af = operand(A, wm * WBM + 16 * i + c);
 #pragma unroll
       for (int t = 0; t < TN; ++t) acc[i][t] = mfma_f8(af, bf[t], acc[i][t]);
     }
@@ -512,7 +519,7 @@ __global__ __launch_bounds__(512) void k_f8_gemm256(LinearArgs a) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 128 + 16 * i + 4 * g + r;
+        const int m = m0 + wm * WBM + 16 * i + 4 * g + r;
         if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16((acc[i][t][r] * s1) * cs + bias);
       }
   }
@@ -571,7 +578,7 @@ hipError_t launch_f8_gemm_tiled(const LinearArgs& a, hipStream_t s) {
     static std::atomic<int> done{0};
     hipError_t e = allow_smem(k_f8_gemm256, kF8Smem, done);
     if (e != hipSuccess) return e;
-    k_f8_gemm256<<<dim3((a.N + kF8T - 1) / kF8T, (a.M + kF8T - 1) / kF8T), 512, kF8Smem, s>>>(a);
+    k_f8_gemm256<<<dim3((a.N + kF8T - 1) / kF8T, (a.M + kF8T - 1) / kF8T), kF8Waves * 64, kF8Smem, s>>>(a);
     return hipGetLastError();
   }
   const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
