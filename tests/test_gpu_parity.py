@@ -182,8 +182,10 @@ def test_linear_mxfp4_m_sweep(M):
 #   ends one step early), 64x64 in 2, 128x64 in 2, 64x128 in 2 (ragged N),
 #   ragged M in 2 groups, 256x256 tiles of 8 waves with ragged M and N (MXFP4,
 #   FP8; INT4 and NVFP4 take 128x128 there)
+# the last two take 256 x 256 tiles (ragged M and N tiles; the last with a
+# partial final K step)
 TILED_CASES = [(256, 1024, 2176), (256, 1024, 2112), (640, 2048, 1152), (384, 4096, 1024), (6144, 192, 1024),
-               (200, 1024, 2048), (3000, 4000, 1024)]
+               (200, 1024, 2048), (3000, 4000, 1024), (2900, 4160, 1120)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)

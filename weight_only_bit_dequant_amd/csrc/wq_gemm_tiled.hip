@@ -326,6 +326,177 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- 256 x 256 tiles
+// For large M x N: one workgroup of NW waves (NW/4 x 4 grid, 256/(NW/4) x 64
+// outputs per wave) owns a 256 x 256 tile; K advances 64 per step.
+// Activation rows go from memory straight into LDS (buffer_load_dwordx4 ...
+// lds writes lane i's 16 bytes at the wave's LDS base + 16 i: one load moves 8
+// whole 128-byte rows, and the row swizzle is applied by choosing which chunk
+// of its row each lane fetches).  The packed weight chunks of step k+2 are
+// loaded into registers during step k, and those of step k+1 are decoded into
+// the other LDS stage at the end of step k.  Two LDS stages of 64 KiB, one
+// barrier per step: after it a wave issues the next step's activation loads
+// and the weight loads two steps ahead, runs its MFMAs, then decodes.
+template <int F, int NW>
+__global__ __launch_bounds__(NW * 64) void k_woq_gemm256(LinearArgs a) {
+  using TF = TileFmt<F>;
+  static_assert(TF::ARS == 128 && TF::BRS == 128, "128-byte LDS rows");
+  constexpr int T = 256, NT = NW * 64;
+  constexpr int WBM = T / (NW / 4), TM = WBM / 16, TN = 4;
+  constexpr int STAGE = 2 * T * 128;                 // A rows then B rows
+  constexpr int XJ = 32 / NW;                        // activation loads (8 rows each) per wave and step
+  constexpr int LB = TF::WSTEP / 16;                 // packed 16-byte chunks per column and step
+  constexpr int CB = T * LB;                         // packed chunks per step
+  constexpr int NB = (CB + NT - 1) / NT;             // per thread
+  constexpr int DB = decoded_bytes<F>();
+  constexpr int kpc = (F == KF_BF16) ? 8 : (F == KF_FP8 ? 16 : 32);  // K per packed chunk
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int M = a.M, N = a.N, K = a.K;
+
+  // XCD-aware tile order (consecutive workgroups go round-robin to the XCDs)
+  const int gx = gridDim.x, G = gx * gridDim.y;
+  int b = blockIdx.y * gx + blockIdx.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int n0 = (b % gx) * T, m0 = (b / gx) * T;
+
+  const uint32_t wrow = (F == KF_BF16) ? 2u * (uint32_t)K : (F == KF_FP8 ? (uint32_t)K : (uint32_t)K / 2u);
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * wrow);
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * (uint32_t)K * 2u);
+  uint32_t sbytes = 0;
+  if constexpr (F == KF_INT4) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 2u;
+  else if constexpr (F == KF_INT4A) sbytes = (uint32_t)N * (uint32_t)(K / 128) * 4u;
+  else if constexpr (F == KF_NVFP4) sbytes = (uint32_t)N * (uint32_t)(K / 16);
+  else if constexpr (F == KF_MXFP4) sbytes = (uint32_t)N * (uint32_t)(K / 32);
+  else if constexpr (F == KF_FP8) sbytes = (uint32_t)N * 4u;
+  const __amdgpu_buffer_rsrc_t Sr = make_rsrc(a.scales ? a.scales : a.W, a.scales ? sbytes : 0u);
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  const int KT = (K + 63) / 64;
+
+  // activation rows (256/NW)*w .. of step kt into LDS stage st; K past the end
+  // and rows past M read zero
+  auto issueX = [&](int kt, int st) {
+    unsigned char* dst0 = smem + st * STAGE + (T / NW) * wave * 128;
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int r = (T / NW) * wave + 8 * j + (lane >> 3);
+      const int kx = kt * 64 + 8 * TF::pos(r, lane & 7);  // the slot map is its own inverse
+      const uint32_t off = off_if(kx < K, ((uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)kx) * 2u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (__attribute__((address_space(3))) void*)(dst0 + j * 1024), 16, off, 0,
+                                               0, 0);
+    }
+  };
+  // packed weight chunks of step kt (threads past the chunk count repeat a
+  // chunk: identical bytes, no divergent branch)
+  u32x4 wb[2][NB];
+  uint32_t sb[2][NB];
+  auto loadW = [&](int kt, u32x4 (&w)[NB], uint32_t (&sc)[NB]) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int id = (q * NT + tid) % CB;
+      const int col = id / LB, part = id % LB;
+      const uint32_t n = (uint32_t)(n0 + col);
+      const int k0 = kt * 64 + part * kpc;
+      const bool ok = k0 < K;
+      const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : (F == KF_FP8 ? (uint32_t)k0 : (uint32_t)k0 / 2u);
+      w[q] = bload128(Wr, off_if(ok, n * wrow + byte0));
+      if constexpr (F == KF_INT4) sc[q] = bload16(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u));
+      else if constexpr (F == KF_INT4A) sc[q] = bload32(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 4u));
+      else if constexpr (F == KF_NVFP4) sc[q] = bload16(Sr, off_if(ok, n * (uint32_t)(K / 16) + (uint32_t)(k0 / 16)));
+      else if constexpr (F == KF_MXFP4) sc[q] = bload8(Sr, off_if(ok, n * (uint32_t)(K / 32) + (uint32_t)(k0 / 32)));
+      else sc[q] = 0u;
+    }
+  };
+  auto decodeW = [&](int st, const u32x4 (&w)[NB], const uint32_t (&sc)[NB]) {
+    unsigned char* B = smem + st * STAGE + T * 128;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int id = (q * NT + tid) % CB;
+      const int col = id / LB, part = id % LB;
+      decode_store<F>(B + col * 128, col, part * (DB / 16), w[q], sc[q]);
+    }
+  };
+
+  uint32_t bias_bits[TN], cs_bits[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const uint32_t n = (uint32_t)(n0 + wn * 64 + 16 * t + c);
+    bias_bits[t] = bload16(Br, n * 2u);
+    cs_bits[t] = (F == KF_FP8) ? bload32(Sr, n * 4u) : 0x3F800000u;
+  }
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int st) {
+    const unsigned char* A = smem + st * STAGE;
+    const unsigned char* B = A + T * 128;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      // lane (g, c): K 32kk + 8g .. +7 of the step = 16-byte chunk 4kk + g
+      bf16x8 bf[TN];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * 64 + 16 * t + c;
+        bf[t] = *reinterpret_cast<const bf16x8*>(B + r * 128 + TF::pos(r, 4 * kk + g) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WBM + 16 * i + c;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(A + r * 128 + TF::pos(r, 4 * kk + g) * 16);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[i][t] = mfma_bf16(af, bf[t], acc[i][t]);
+      }
+    }
+  };
+
+  // steps past K read zeros and add nothing: the step count is padded to an
+  // even number so that both register stages are compile-time indices
+  const int KTP = (KT + 1) / 2 * 2;
+  issueX(0, 0);
+  loadW(0, wb[0], sb[0]);
+  loadW(1, wb[1], sb[1]);
+  decodeW(0, wb[0], sb[0]);
+  for (int kt = 0; kt < KTP; kt += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // this wave's loads are done: activations of step kt+h in LDS, weight
+      // registers of step kt+h+1; after the barrier every wave's are, and
+      // stage (kt+h+1)&1 is no longer read
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      issueX(kt + h + 1, (h + 1) & 1);
+      loadW(kt + h + 2, wb[h], sb[h]);
+      compute(h);
+      decodeW((h + 1) & 1, wb[(h + 1) & 1], sb[(h + 1) & 1]);
+    }
+  }
+  // no LDS write may still be in flight when the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  float s1 = 1.0f;
+  if constexpr (F == KF_NVFP4) s1 = a.gscale[0];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int n = n0 + wn * 64 + 16 * t + c;
+    const float bias = bitsf(bias_bits[t] << 16), cs = bitsf(cs_bits[t]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * WBM + 16 * i + 4 * g + r;
+        const float y = (F == KF_FP8) ? acc[i][t][r] * cs : acc[i][t][r] * s1;
+        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
+      }
+  }
+}
+
 template <int F, int BM, int BN, int KS, int WGN = 2>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   constexpr int sm = KS * tile_smem<F, BM, BN>();
@@ -340,12 +511,22 @@ hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 8 waves of 128 x 64 outputs: with 16 waves of 64 x 64 every format spilled
+// registers (128 per wave at four waves per SIMD)
+constexpr int kWoqWaves = 8;
+
 template <int F>
 hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  // 128 x 128 tiles are planned only when there are enough of them (no K
-  // groups); the other shapes run with one or two K groups
-  if constexpr (F == KF_MXFP4 || F == KF_FP8) {
-    if (p.bm == 256) return launch_tile<F, 256, 256, 1, 4>(a, s);
+  // 256 x 256 and 128 x 128 tiles are planned only when there are enough of
+  // them (no K groups); the other shapes run with one or two K groups
+  if (p.bm == 256) {
+    static std::atomic<int> done{0};
+    constexpr int sm = 2 * 2 * 256 * 128;
+    auto k = k_woq_gemm256<F, kWoqWaves>;
+    hipError_t e = allow_smem(k, sm, done);
+    if (e != hipSuccess) return e;
+    k<<<dim3((a.N + 255) / 256, (a.M + 255) / 256), kWoqWaves * 64, sm, s>>>(a);
+    return hipGetLastError();
   }
   if (p.bm == 128 && p.bn == 128) return launch_tile<F, 128, 128, 1>(a, s);
   if (p.bm == 128) return p.ks >= 2 ? launch_tile<F, 128, 64, 2>(a, s) : launch_tile<F, 128, 64, 1>(a, s);

@@ -439,13 +439,12 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
     p.S = 1;
     p.bm = 64;
     p.bn = 64;
-    // 256 x 256 tiles (8 waves) only where the decode is light enough to fit
-    // the registers of two waves per SIMD without spilling (MXFP4, FP8); the
-    // INT4 and NVFP4 decodes spill there and run 128 x 128.
-    const bool big_ok = kfmt == KF_MXFP4 || kfmt == KF_FP8;
+    // 256 x 256 tiles: k_woq_gemm256 (activations loaded straight into LDS);
+    // measured at M = 4096 (N = 4096, K = 3072): INT4 157 -> 114 us against
+    // 128 x 128 tiles, MXFP4 and FP8 on par with the register-staged 256 x 256
+    // kernel it replaced.
     const int cand[4][2] = {{256, 256}, {128, 128}, {128, 64}, {64, 128}};
     for (const auto& cb : cand) {
-      if (cb[0] == 256 && !big_ok) continue;
       const int64_t tiles = ((M + cb[0] - 1) / cb[0]) * ((N + cb[1] - 1) / cb[1]);
       if (tiles >= 192) {
         p.bm = cb[0];
