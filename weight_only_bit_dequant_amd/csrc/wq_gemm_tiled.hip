@@ -497,6 +497,148 @@ __global__ __launch_bounds__(NW * 64) void k_woq_gemm256(LinearArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- MXFP4, 256 x 256 tiles, weights in registers
+// For large M x N: one workgroup of 8 waves (2 x 4 grid, 128 x 64 outputs per
+// wave) owns a 256 x 256 tile and K advances 128 per step, twice the K per
+// barrier of k_woq_gemm256: only the activations pass through LDS (256 rows x
+// 256 bytes per step, loaded straight into LDS), while every wave loads and
+// decodes its own 64 weight columns in registers.  Lane (g, c) of a wave holds
+// K 32g .. 32g+31 of the step for its columns (16 packed bytes and their E8M0
+// scale) and, in sub-step kk, feeds K 32g + 8kk .. +7 to the MFMA; it reads
+// the activations with the same K order (16-byte chunk 4g + kk of the row).
+// The two waves of a column block load the same weight bytes (from L1) and
+// decode them twice.  Measured at M = 4096 (N = 4096, K = 3072): 98-102 us
+// against 104-107 us for k_woq_gemm256.  The same scheme spilled registers for
+// the other formats (their decodes need more), which stay on k_woq_gemm256.
+struct MxWReg {
+  uint32_t w[4];  // 32 E2M1 codes, K order, low nibble first
+  uint32_t sc;    // E8M0 scale byte of the 32-element block
+};
+
+__device__ __forceinline__ void mxwreg_load(MxWReg& r, __amdgpu_buffer_rsrc_t Wr, __amdgpu_buffer_rsrc_t Sr, uint32_t n,
+                                            int kb, int K) {
+  const bool ok = kb < K;
+  const u32x4 v = bload128(Wr, off_if(ok, n * ((uint32_t)K / 2u) + (uint32_t)kb / 2u));
+  r.w[0] = v.x;
+  r.w[1] = v.y;
+  r.w[2] = v.z;
+  r.w[3] = v.w;
+  r.sc = bload8(Sr, off_if(ok, n * (uint32_t)(K / 32) + (uint32_t)(kb / 32)));
+}
+
+// LDS slot of 16-byte chunk k (0..15) of activation row r (256-byte rows): the
+// 16 reads of rows c = 0..7 by lane groups g and g+1 (chunks 4g + kk) land on
+// 16 distinct 16-byte bank groups
+__device__ __forceinline__ int wreg_pos(int r, int k) { return k ^ ((r & 3) | (((r >> 2) & 1) << 3)); }
+
+__global__ __launch_bounds__(512) void k_mx_wreg(LinearArgs a) {
+  constexpr int T = 256, TM = 8, TN = 4;
+  constexpr int STAGE = T * 256;  // activation rows of one step
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int M = a.M, N = a.N, K = a.K;
+
+  // XCD-aware tile order (consecutive workgroups go round-robin to the XCDs)
+  const int gx = gridDim.x, G = gx * gridDim.y;
+  int b = blockIdx.y * gx + blockIdx.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int n0 = (b % gx) * T, m0 = (b / gx) * T;
+
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * ((uint32_t)K / 2u));
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t Sr = make_rsrc(a.scales, (uint32_t)N * (uint32_t)(K / 32));
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  const int KT = (K + 127) / 128;
+
+  // activation rows 32w .. 32w+31 of step kt into LDS stage st: load j moves
+  // rows +4j .. +4j+3, lane L filling slot L % 16 of row L / 16 with the chunk
+  // stored there (the slot map is its own inverse); K past the end and rows
+  // past M read zero
+  auto issueX = [&](int kt, int st) {
+    unsigned char* dst0 = smem + st * STAGE + 32 * wave * 256;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 32 * wave + 4 * j + (lane >> 4);
+      const int kx = kt * 128 + 8 * wreg_pos(r, lane & 15);
+      const uint32_t off = off_if(kx < K, ((uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)kx) * 2u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (__attribute__((address_space(3))) void*)(dst0 + j * 1024), 16, off, 0,
+                                               0, 0);
+    }
+  };
+  MxWReg wr[2][TN];
+  auto loadW = [&](int kt, MxWReg (&r)[TN]) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+      mxwreg_load(r[t], Wr, Sr, (uint32_t)(n0 + wn * 64 + 16 * t + c), kt * 128 + 32 * g, K);
+  };
+
+  uint32_t bias_bits[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) bias_bits[t] = bload16(Br, (uint32_t)(n0 + wn * 64 + 16 * t + c) * 2u);
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int st, const MxWReg (&r)[TN]) {
+    const unsigned char* A = smem + st * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 bf[TN];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) bf[t] = dec_fp4_pow2(r[t].w[kk], e8m0_decode(r[t].sc & 0xFFu));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * 128 + 16 * i + c;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(A + row * 256 + wreg_pos(row, 4 * g + kk) * 16);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[i][t] = mfma_bf16(af, bf[t], acc[i][t]);
+      }
+      // keep each sub-step's decode and operand reads next to its MFMAs
+      // (hoisting them all over-commits the registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // steps past K read zeros and add nothing; the step count is padded to an
+  // even number so that both register stages are compile-time indices
+  const int KTP = (KT + 1) / 2 * 2;
+  issueX(0, 0);
+  loadW(0, wr[0]);
+  for (int kt = 0; kt < KTP; kt += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // this wave's loads of step kt+h are done; after the barrier every
+      // wave's are, and stage (kt+h+1)&1 is no longer read
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      issueX(kt + h + 1, (h + 1) & 1);
+      loadW(kt + h + 1, wr[(h + 1) & 1]);
+      compute(h, wr[h]);
+    }
+  }
+  // no LDS write may still be in flight when the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int n = n0 + wn * 64 + 16 * t + c;
+    const float bias = bitsf(bias_bits[t] << 16);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 128 + 16 * i + 4 * g + r;
+        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][t][r] + bias);
+      }
+  }
+}
+
 template <int F, int BM, int BN, int KS, int WGN = 2>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   constexpr int sm = KS * tile_smem<F, BM, BN>();
@@ -519,6 +661,17 @@ template <int F>
 hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   // 256 x 256 and 128 x 128 tiles are planned only when there are enough of
   // them (no K groups); the other shapes run with one or two K groups
+  if constexpr (F == KF_MXFP4) {
+    if (p.bm == 256) {
+      static std::atomic<int> done{0};
+      constexpr int sm = 2 * 256 * 256;
+      auto k = k_mx_wreg;
+      hipError_t e = allow_smem(k, sm, done);
+      if (e != hipSuccess) return e;
+      k<<<dim3((a.N + 255) / 256, (a.M + 255) / 256), 512, sm, s>>>(a);
+      return hipGetLastError();
+    }
+  }
   if (p.bm == 256) {
     static std::atomic<int> done{0};
     constexpr int sm = 2 * 2 * 256 * 128;
