@@ -187,7 +187,8 @@ wq_status wq_fp8_scale(const float* amax, float* scale, int64_t count, void* str
  * Static activation Q ("TorchAO Static FP8 Quantization (Linear)", intro and
  * "Graph after export" figure: bf16 activation -> Q -> FP8):
  * Xq = E4M3(clamp(fp32(x / act_scale), +-448)), nearest-even; act_scale is one
- * device float.  X bf16 [M][K] -> Xq uint8 [M][K].
+ * device float (0 keeps x).  X bf16 [M][K] -> Xq uint8 [M][K]; M * K < 2^43
+ * (else WQ_EUNSUPPORTED).
  */
 wq_status wq_fp8_quantize_act(const void* X, int64_t M, int64_t K, const float* act_scale, void* Xq,
                               void* stream);
@@ -231,10 +232,10 @@ wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_s
  * with the same per-step arithmetic as two wq_fp8_static_linear calls (results
  * differ only by fp32 accumulation order); H never leaves the chip.
  * W1q E4M3 [N1][K1], W2q E4M3 [N2][N1], scales float [N1] / [N2], biases bf16
- * or NULL.  K1 % 16 == 0, N1 % 16 == 0, and 16 rows of the input and hidden
- * codes plus both layers' column scales and biases must fit in the 160 KiB LDS
- * of a CU (K1 + N1 up to about 9.5K; else WQ_EUNSUPPORTED -- use two
- * wq_fp8_static_linear calls).  No workspace.
+ * or NULL.  K1 % 16 == 0, N1 % 16 == 0, M * K1 * 2 < 2^31, and 16 rows of the
+ * input and hidden codes plus both layers' column scales and biases must fit
+ * in the 160 KiB LDS of a CU (K1 + N1 up to about 9.5K; else WQ_EUNSUPPORTED --
+ * use two wq_fp8_static_linear calls).  No workspace.
  */
 wq_status wq_fp8_static_mlp2(const void* X, int64_t M, int64_t K1, const float* act_scale1, const void* W1q,
                              const float* w1_scale, const void* b1, int64_t N1, const float* act_scale2,

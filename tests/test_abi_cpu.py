@@ -101,6 +101,7 @@ def test_quantize_pack_dequant_validation():
     assert L.wq_dequantize(3, v(16), v(16), None, 64, 64, v(16), None) == wq.EINVAL
     assert L.wq_dequantize(2, v(16), v(16), None, 64, 12, v(16), None) == wq.EUNSUPPORTED
     assert L.wq_fp8_quantize_act(v(16), 4, 16, None, v(16), None) == wq.EINVAL
+    assert L.wq_fp8_quantize_act(v(16), 1 << 22, 1 << 21, v(16), v(16), None) == wq.EUNSUPPORTED  # 2^43 elements
     assert L.wq_fp8_static_linear(v(16), 4, 24, v(16), v(16), v(16), None, 16, v(16), v(16), 1 << 20,
                                   None) == wq.EUNSUPPORTED
     assert L.wq_fp8_static_linear(v(16), 4, 32, v(16), v(16), v(16), None, 16, v(16), None, 0,
@@ -135,6 +136,7 @@ def test_quantize_pack_dequant_validation():
     assert mlp(N1=40) == wq.EUNSUPPORTED
     assert mlp(K1=8192, N1=4096) == wq.EUNSUPPORTED  # 16 rows exceed the LDS
     assert mlp(X=8) == wq.EALIGN
+    assert mlp(M=1 << 20, K1=1024, N1=256, N2=64) == wq.EUNSUPPORTED  # activation buffer of 2^31 bytes
     assert mlp(M=0) == wq.OK
     # read-only stream (measurement aid)
     assert L.wq_read_stream(v(16), 0, None, None) == wq.OK
