@@ -74,7 +74,8 @@ def test_mx_quantize_act_bit_exact(M, K):
 @pytest.mark.parametrize("M,N,K,bias", [(1, 4096, 3072, True), (17, 256, 512, True), (32, 4096, 3072, True),
                                         (33, 224, 96, False), (64, 512, 1024, True), (100, 128, 256, True),
                                         (200, 256, 160, True), (256, 4096, 3072, True), (4096, 4096, 3072, True),
-                                        (300, 512, 1536, False), (1024, 1024, 2560, True)])
+                                        (300, 512, 1536, False), (1024, 1024, 2560, True),
+                                        (3000, 4160, 3200, True), (3000, 4160, 1056, False)])
 def test_mx_linear_vs_oracle(M, N, K, bias):
     W, b, X = synth.linear_case(N, K, M, cfg=90 + M)
     b = b if bias else None
@@ -85,10 +86,13 @@ def test_mx_linear_vs_oracle(M, N, K, bias):
     torch.cuda.synchronize()
     wc, ws = Q.quantize_mxfp4(W)
     assert np.array_equal(host(q["scales"]), ws)
-    # M > 64 runs the tiled kernel (64x64 or 128x128 tiles, a partial last K
-    # step when K % 128 != 0; scale rows preloaded to LDS when K % 512 == 0,
-    # else per step, and an odd step count for K = 1536); very large M is
-    # checked on a sample of rows
+    # M > 64 runs the tiled kernels: 256x256 tiles straight into LDS when
+    # there are >= 192 of them and K % 128 == 0 (ragged M and N tiles and a
+    # half-filled last 256-K step at 3000 x 4160 x 3200), else 64x64 or
+    # 128x128 tiles through registers (a partial last K step when
+    # K % 128 != 0; scale rows preloaded to LDS when K % 512 == 0, else per
+    # step, and an odd step count for K = 1536); very large M is checked on a
+    # sample of rows
     rows = np.arange(M) if M <= 512 else np.arange(0, M, 61)
     assert_close(Y[torch.as_tensor(rows, device=DEV)], MX.forward(X[rows], wc, ws, b), f"mx M={M} N={N} K={K}")
 

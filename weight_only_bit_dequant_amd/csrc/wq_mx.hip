@@ -411,7 +411,7 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
 // reads its operands and runs its 16 MFMAs.
 constexpr int kF8T = 256;                 // tile rows and columns
 constexpr int kF8Stage = 2 * kF8T * 128;  // one LDS stage: A then B, 128 codes per row
-constexpr int kF8Smem = 2 * kF8Stage;
+constexpr int kF8Smem = 2 * kF8Stage + kF8T * 8;  // + the tile's column scales and biases
 
 // LDS slot of 16-byte chunk k (0..7) of tile row r.  An operand read has lane
 // (g, c) take chunks 2g and 2g+1 of row c; a ds_read_b128 serves lanes 0-7
@@ -471,13 +471,6 @@ __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
     }
   };
 
-  uint32_t bias_bits[TN], cs_bits[TN];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    const uint32_t n = (uint32_t)(n0 + wn * 64 + 16 * t + c);
-    bias_bits[t] = bload16(Br, n * 2u);
-    cs_bits[t] = bload32(Sr, n * 4u);
-  }
   const float s1 = a.act_scale[0];
 
   f32x4 acc[TM][TN];
@@ -494,6 +487,13 @@ __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
   };
 
   issue(0, 0);
+  // the tile's column scales and biases wait in LDS for the epilogue (the
+  // loop's first barrier publishes them; issued after the first step's loads), which keeps registers free
+  float* colv = reinterpret_cast<float*>(smem + 2 * kF8Stage);  // [0][256] scale, [1][256] bias
+  if (tid < kF8T) {
+    colv[tid] = bitsf(bload32(Sr, (uint32_t)(n0 + tid) * 4u));
+    colv[kF8T + tid] = bitsf(bload16(Br, (uint32_t)(n0 + tid) * 2u) << 16);
+  }
   for (int kt = 0; kt < KT; ++kt) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of step kt are in LDS
     __syncthreads();                     // ... and every wave's; stage (kt+1)&1 is no longer read
@@ -514,13 +514,138 @@ __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int n = n0 + wn * 64 + 16 * t + c;
-    const float bias = bitsf(bias_bits[t] << 16), cs = bitsf(cs_bits[t]);
+    const float cs = colv[wn * 64 + 16 * t + c], bias = colv[kF8T + wn * 64 + 16 * t + c];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * WBM + 16 * i + 4 * g + r;
         if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16((acc[i][t][r] * s1) * cs + bias);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- MXFP4 x MXFP4, 256 x 256 tiles
+// For large M x N: 16 waves (4 x 4 grid, 64 x 64 outputs per wave) own a
+// 256 x 256 tile and K advances 256 per step: two scaled MFMAs deep, twice the
+// K per barrier of the E4M3 kernel above at the same LDS stage size (128
+// packed bytes per row).  Packed rows and their E8M0 scale bytes go from
+// memory straight into LDS (buffer_load_dwordx4 / buffer_load_dword ... lds;
+// lane i's bytes land at the wave's LDS base + 16 i or 4 i).  Stage layout:
+// activation codes [256][128], weight codes [256][128], activation scales
+// [256][8], weight scales [256][8]; two stages.  Needs K % 128 == 0 (whole
+// scale dwords per row) and 4-byte aligned scale arrays.
+constexpr int kMxT = 256;
+constexpr int kMxCodes = kMxT * 128;                  // one operand's codes per step
+constexpr int kMxStage = 2 * kMxCodes + 2 * kMxT * 8;  // codes, then scales
+constexpr int kMxSmem = 2 * kMxStage + kMxT * 4;  // + the tile's biases
+
+__global__ __launch_bounds__(1024) void k_mx_gemm256(LinearArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int TM = 4, TN = 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int M = a.M, N = a.N, K = a.K;
+
+  // XCD-aware tile order (see the bf16 tiled kernel)
+  const int gx = gridDim.x, G = gx * gridDim.y;
+  int b = blockIdx.y * gx + blockIdx.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int n0 = (b % gx) * kMxT, m0 = (b / gx) * kMxT;
+
+  const uint32_t rowb = (uint32_t)K / 2u, srow = (uint32_t)K / 32u;
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * rowb);
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * rowb);
+  const __amdgpu_buffer_rsrc_t Xsr = make_rsrc(a.xscales, (uint32_t)M * srow);
+  const __amdgpu_buffer_rsrc_t Wsr = make_rsrc(a.scales, (uint32_t)N * srow);
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  const int KT = (K + 255) / 256;
+
+  // waves 0-7 load activation rows 32w .., waves 8-15 weight rows 32(w-8) ..:
+  // four code loads of 8 rows (lane L fills slot L % 8 of row L / 8 with the
+  // chunk stored there; the slot map is its own inverse) and one scale load
+  // (lane L: dword L % 2 of row L / 2's 8 scale bytes); K past the end and
+  // rows past M / N read zero
+  const bool loadA = wave < 8;
+  const __amdgpu_buffer_rsrc_t Lr = loadA ? Xr : Wr;
+  const __amdgpu_buffer_rsrc_t Lsr = loadA ? Xsr : Wsr;
+  const int lrow0 = 32 * (wave & 7);
+  const uint32_t lbase = (uint32_t)((loadA ? m0 : n0) + lrow0);
+  auto issue = [&](int kt, int st) {
+    unsigned char* base = smem + st * kMxStage;
+    unsigned char* dst0 = base + (loadA ? 0 : kMxCodes) + lrow0 * 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = lrow0 + 8 * j + (lane >> 3);
+      const int kc = (lane & 7) ^ (r & 7);
+      const bool ok = kt * 256 + 32 * kc < K;
+      const uint32_t off = off_if(ok, (lbase + 8u * j + (uint32_t)(lane >> 3)) * rowb + (uint32_t)kt * 128u + 16u * kc);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Lr, (__attribute__((address_space(3))) void*)(dst0 + j * 1024), 16, off, 0,
+                                               0, 0);
+    }
+    const int h = lane & 1;
+    const bool sok = kt * 8 + 4 * h < (int)srow;
+    const uint32_t soff = off_if(sok, (lbase + (uint32_t)(lane >> 1)) * srow + (uint32_t)kt * 8u + 4u * h);
+    unsigned char* sdst = base + 2 * kMxCodes + (loadA ? 0 : kMxT * 8) + lrow0 * 8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(Lsr, (__attribute__((address_space(3))) void*)sdst, 4, soff, 0, 0, 0);
+  };
+
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  // the tile's biases wait in LDS for the epilogue (the loop's first barrier
+  // publishes them), which keeps registers free
+  float* colb = reinterpret_cast<float*>(smem + 2 * kMxStage);
+  if (tid < kMxT) colb[tid] = bitsf(bload16(Br, (uint32_t)(n0 + tid) * 2u) << 16);
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of step kt are in LDS
+    __syncthreads();                     // ... and every wave's; stage (kt+1)&1 is no longer read
+    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
+    const unsigned char* base = smem + (kt & 1) * kMxStage;
+    const unsigned char* A = base;
+    const unsigned char* B = base + kMxCodes;
+    const unsigned char* AS = base + 2 * kMxCodes;
+    const unsigned char* BS = AS + kMxT * 8;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      // lane (g, c): row/column c, K 128 s2 + 32g .. +31 = chunk 4 s2 + g of
+      // the row and scale byte 4 s2 + g
+      u32x4 bf[TN];
+      uint32_t bs[TN];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * 64 + 16 * t + c;
+        bf[t] = *reinterpret_cast<const u32x4*>(B + r * 128 + ((4 * s2 + g) ^ (r & 7)) * 16);
+        bs[t] = BS[r * 8 + 4 * s2 + g];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * 64 + 16 * i + c;
+        const u32x4 af = *reinterpret_cast<const u32x4*>(A + r * 128 + ((4 * s2 + g) ^ (r & 7)) * 16);
+        const uint32_t as = AS[r * 8 + 4 * s2 + g];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[i][t] = mfma_mx4(af, as, bf[t], bs[t], acc[i][t]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int n = n0 + wn * 64 + 16 * t + c;
+    const float bias = colb[wn * 64 + 16 * t + c];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 64 + 16 * i + 4 * g + r;
+        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][t][r] + bias);
       }
   }
 }
@@ -587,9 +712,18 @@ hipError_t launch_f8_gemm_tiled(const LinearArgs& a, hipStream_t s) {
 
 hipError_t launch_mx_linear(const LinearArgs& a, hipStream_t s) {
   if (a.M > 64) {
-    // matrix-core bound: 128 x 128 tiles when they fill the chip, else 64 x 64
-    // (measured: 128 x 256 tiles of 8 waves ran no faster at M = 4096, and
-    // 256 x 256 spilled registers)
+    // matrix-core bound: 256 x 256 tiles straight into LDS when they fill the
+    // chip (whole scale dwords per row needed), else 128 x 128 or 64 x 64
+    // through registers
+    const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
+    if (t256 >= 192 && a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.xscales) & 3) == 0 &&
+        (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0) {
+      static std::atomic<int> done{0};
+      hipError_t e = allow_smem(k_mx_gemm256, kMxSmem, done);
+      if (e != hipSuccess) return e;
+      k_mx_gemm256<<<dim3((a.N + kMxT - 1) / kMxT, (a.M + kMxT - 1) / kMxT), 1024, kMxSmem, s>>>(a);
+      return hipGetLastError();
+    }
     const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
 
     return t128 >= 192 ? launch_mx_tile<128, 128>(a, s) : launch_mx_tile<64, 64>(a, s);
