@@ -109,3 +109,30 @@ def test_mx_two_calls_equal_one_call():
     torch.cuda.synchronize()
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
     assert torch.equal(Y1.view(torch.int16), Y3.view(torch.int16))
+
+
+def test_mx_large_tiles_with_unaligned_scales():
+    """The 256 x 256 kernel loads scale rows as dwords; with scale arrays that
+    are not 4-byte aligned the call takes the register-staged kernel instead.
+    Both give the same bits."""
+    M, N, K = 2048, 6144, 1024  # 8 x 24 = 192 tiles of 256 x 256
+    W, b, X = synth.linear_case(N, K, M, cfg=33)
+    print(f"[case] mx large tiles, unaligned scales M={M} N={N} K={K}", flush=True)
+    q = wq.quantize("mxfp4", dev_bf16(W))
+    Xd, bd = dev_bf16(X), dev_bf16(b)
+    Xq, Xs = wq.mx_quantize_act(Xd)
+    Y1 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    wq.wq_mx_linear(Xq, Xs, K, q["packed"], q["scales"], bd, N, Y1)
+    # the same scale bytes at an odd address
+    xs_odd = torch.empty(Xs.numel() + 1, dtype=torch.uint8, device=DEV)[1:].view(Xs.shape)
+    xs_odd.copy_(Xs)
+    ws_odd = torch.empty(q["scales"].numel() + 1, dtype=torch.uint8, device=DEV)[1:].view(q["scales"].shape)
+    ws_odd.copy_(q["scales"])
+    Y2 = torch.empty_like(Y1)
+    wq.wq_mx_linear(Xq, xs_odd, K, q["packed"], ws_odd, bd, N, Y2)
+    torch.cuda.synchronize()
+    rows = np.arange(0, M, 67)
+    wc, ws = Q.quantize_mxfp4(W)
+    ref = MX.forward(X[rows], wc, ws, b)
+    assert_close(Y1[torch.as_tensor(rows, device=DEV)], ref, "mx 256 tiles")
+    assert_close(Y2[torch.as_tensor(rows, device=DEV)], ref, "mx unaligned scales")
