@@ -126,7 +126,9 @@ def test_dequantize_bf16_bit_exact(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,N,K", [(1, 128, 256), (17, 256, 512), (32, 192, 384), (33, 320, 768),
+# (2, 4096, 3072): the one- and two-row kernel that loads activations in the
+# operand layout directly (256 workgroups, no split)
+@pytest.mark.parametrize("M,N,K", [(1, 128, 256), (2, 4096, 3072), (17, 256, 512), (32, 192, 384), (33, 320, 768),
                                    (64, 256, 1024), (100, 128, 256)])
 def test_linear_small_shapes(fmt, M, N, K):
     W, b, X = synth.linear_case(N, K, M, cfg=20 + M)
@@ -326,8 +328,8 @@ def test_static_large_layer(M):
     assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"static 3072->4096 M={M}")
 
 
-@pytest.mark.parametrize("M,N,K,bias", [(32, 4096, 3072, False), (17, 200, 512, True), (64, 256, 1024, True),
-                                        (256, 4096, 3072, False), (640, 2048, 1152, True)])
+@pytest.mark.parametrize("M,N,K,bias", [(32, 4096, 3072, False), (2, 4096, 3072, True), (17, 200, 512, True),
+                                        (64, 256, 1024, True), (256, 4096, 3072, False), (640, 2048, 1152, True)])
 def test_fp8_linear_on_prequantized_activations(M, N, K, bias):
     """wq_fp8_quantize_act then wq_fp8_linear equals wq_fp8_static_linear bit
     for bit (same kernels) and the oracle's fp64 DQ-GEMM within the bar."""
