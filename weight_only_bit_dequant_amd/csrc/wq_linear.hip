@@ -394,14 +394,21 @@ hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
     constexpr int sm = smem_bytes<F, MT, 4, 4>(false);
     k_linear<F, MT, 4, 4, spw_split<F>(), false><<<grid, 256, sm, s>>>(a, p.S);
     if (p.S > 1) k_splitk_reduce<F, MT, 4, 4><<<dim3(p.gx, 1, p.gz), 256, 0, s>>>(a, p.S);
-  } else if (MT == 1 && a.M <= 2) {
-    // one or two rows: the activation slice is a few KiB, and loading it in the
-    // operand layout directly beats staging it through LDS (measured at
-    // N = 4096, K = 3072, MXFP4: M = 1 5.0 against 5.2 us, M = 2 5.2 against
-    // 5.3 us; from four rows up the staging wins)
-    constexpr int sm = smem_bytes<F, MT, 1, 12>(false);
-    k_linear<F, MT, 1, 12, spw_nosplit<F>(), false><<<grid, 768, sm, s>>>(a, p.S);
   } else {
+    if constexpr (MT == 1) {
+      if (a.M <= 2) {
+        // one or two rows: the activation slice is a few KiB, and loading it
+        // in the operand layout directly beats staging it through LDS; with
+        // so little work per column tile, 6 waves of twice the K beat 12
+        // (measured at N = 4096, K = 3072, MXFP4, M = 1, weights in cache:
+        // 12 waves staged 5.2 us, direct 5.0 us, 6 waves direct 4.5 us; with
+        // cold weights both direct forms take 4.8 us; from four rows up the
+        // 12 staged waves win)
+        constexpr int sm = smem_bytes<F, MT, 1, 6>(false);
+        k_linear<F, MT, 1, 6, 2 * spw_nosplit<F>(), false><<<grid, 384, sm, s>>>(a, p.S);
+        return hipGetLastError();
+      }
+    }
     // no-split tiles with activations staged through LDS
     constexpr int sm = smem_bytes<F, MT, 1, 12>(true);
     static_assert(sm <= 160 * 1024, "no-split tile exceeds the LDS of a CU");
