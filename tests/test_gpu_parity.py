@@ -136,6 +136,16 @@ def test_linear_small_shapes(fmt, M, N, K):
     assert_close(Y, oracle_linear(fmt, W, b, X), f"{fmt} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("fmt,N", [("int4", 4100), ("fp8", 4100), ("nvfp4", 4112), ("mxfp4", 4128), ("int4_asym", 4100)])
+@pytest.mark.parametrize("M", [40, 64])
+def test_linear_two_row_blocks_wide(fmt, N, M):
+    # 33..64 rows on a wide layer: two row blocks of 32-column workgroups
+    # (256 and more of them), with a column tail inside the last tile
+    W, b, X = synth.linear_case(N, 512, M, cfg=36 + M)
+    _, Y = run_linear(fmt, W, b, X)
+    assert_close(Y, oracle_linear(fmt, W, b, X), f"{fmt} M={M} N={N}")
+
+
 @pytest.mark.parametrize("fmt,N", [("int4", 200), ("fp8", 200), ("nvfp4", 208), ("mxfp4", 224), ("int4_asym", 200)])
 def test_linear_ragged_n(fmt, N):
     # column tail that does not fill the 64-column workgroup tile
@@ -329,7 +339,8 @@ def test_static_large_layer(M):
 
 
 @pytest.mark.parametrize("M,N,K,bias", [(32, 4096, 3072, False), (2, 4096, 3072, True), (17, 200, 512, True),
-                                        (64, 256, 1024, True), (256, 4096, 3072, False), (640, 2048, 1152, True)])
+                                        (64, 256, 1024, True), (48, 4112, 1024, True), (256, 4096, 3072, False),
+                                        (640, 2048, 1152, True)])
 def test_fp8_linear_on_prequantized_activations(M, N, K, bias):
     """wq_fp8_quantize_act then wq_fp8_linear equals wq_fp8_static_linear bit
     for bit (same kernels) and the oracle's fp64 DQ-GEMM within the bar."""

@@ -6,12 +6,13 @@
 // scale).  The static-FP8 page's intro runs the GEMM itself in FP8.  Here:
 //
 //  * no-split tiles (wide layers): one workgroup = 12 waves = 16 output
-//    columns x all of K; each wave owns a contiguous K range (split-K inside
-//    the workgroup).  Split tiles (narrow layers): 4 waves = 64 columns x a K
+//    columns (32 for two row blocks) x all of K; each wave owns a contiguous
+//    K range (split-K inside the workgroup).  Split tiles (narrow layers): 4 waves = 64 columns x a K
 //    range, with the K ranges of one column tile spread over S workgroups;
-//  * each wave issues every load of its K range (packed weight, block scales,
-//    activations, bias, column scale) before the first wait, as buffer loads
-//    whose out-of-range offsets read zero (no branches around loads);
+//  * each wave issues every load of its K range (activations first, then
+//    packed weights and block scales; bias and column scale at the start)
+//    before the first wait, as buffer loads whose out-of-range offsets read
+//    zero (no branches around loads);
 //  * activations (M <= 32 rows per workgroup) are loaded with contiguous
 //    16-byte loads into a private LDS slot per wave and read back in the
 //    MFMA operand layout;
@@ -144,7 +145,10 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
 
   const int wi = split * NW + wave;
   for (int blk = wi; blk * SPW < T; blk += S * NW) {
-    // ---- issue every load of this block before any wait
+    // ---- issue every load of this block before any wait: the activation
+    // slices first (cache hits; loads return in issue order, so their LDS
+    // staging can start while the weight stream is still in flight), then
+    // the packed weights and block scales
     u32x4 w[SPW][NTW];
     u32x4 xv[SPW][MT][XL];
     uint32_t sc[SPW][NTW];
@@ -152,16 +156,6 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     for (int st = 0; st < SPW; ++st) {
       const int kl = (blk * SPW + st) * MACRO + g * KPL;
       const bool kv = kl < K;
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const uint32_t n = (uint32_t)(n0 + 16 * t + c);
-        w[st][t] = bload128(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
-        if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u));
-        else if constexpr (F == KF_INT4A) sc[st][t] = bload32(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 4u));
-        else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, off_if(kv, n * (uint32_t)(K / 16) + (uint32_t)(kl / 16)));
-        else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, off_if(kv, n * (uint32_t)(K / 32) + (uint32_t)(kl / 32)));
-        else sc[st][t] = 0u;
-      }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const uint32_t m = (uint32_t)(m0 + 16 * i + c);
@@ -181,6 +175,25 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
         }
       }
     }
+#pragma unroll
+    for (int st = 0; st < SPW; ++st) {
+      const int kl = (blk * SPW + st) * MACRO + g * KPL;
+      const bool kv = kl < K;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const uint32_t n = (uint32_t)(n0 + 16 * t + c);
+        w[st][t] = bload128(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
+        if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u));
+        else if constexpr (F == KF_INT4A) sc[st][t] = bload32(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 4u));
+        else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, off_if(kv, n * (uint32_t)(K / 16) + (uint32_t)(kl / 16)));
+        else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, off_if(kv, n * (uint32_t)(K / 32) + (uint32_t)(kl / 32)));
+        else sc[st][t] = 0u;
+      }
+    }
+    // Keep every load above in flight together: left alone, the scheduler
+    // sinks them towards their uses to save registers, which leaves only 6-10
+    // of the ~20 loads of a wave outstanding at a time.
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- decode and multiply
 #pragma unroll
@@ -387,6 +400,18 @@ constexpr int spw_split() {
   return (F == KF_BF16) ? 4 : ((F == KF_FP8 || F == KF_FP8S) ? 2 : 1);
 }
 
+template <int F, int MT, int NTW>
+hipError_t launch_nosplit(const LinearArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int sm = smem_bytes<F, MT, NTW, 12>(true);
+  static_assert(sm <= 160 * 1024, "no-split tile exceeds the LDS of a CU");
+  static std::atomic<int> done{0};
+  auto k = k_linear<F, MT, NTW, 12, spw_nosplit<F>(), true>;
+  hipError_t e = allow_smem(k, sm, done);
+  if (e != hipSuccess) return e;
+  k<<<grid, 768, sm, s>>>(a, 1);
+  return hipGetLastError();
+}
+
 template <int F, int MT>
 hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   dim3 grid(p.gx, p.S, p.gz);
@@ -410,13 +435,10 @@ hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
       }
     }
     // no-split tiles with activations staged through LDS
-    constexpr int sm = smem_bytes<F, MT, 1, 12>(true);
-    static_assert(sm <= 160 * 1024, "no-split tile exceeds the LDS of a CU");
-    static std::atomic<int> done{0};
-    auto k = k_linear<F, MT, 1, 12, spw_nosplit<F>(), true>;
-    hipError_t e = allow_smem(k, sm, done);
-    if (e != hipSuccess) return e;
-    k<<<grid, 768, sm, s>>>(a, p.S);
+    if constexpr (MT == 2) {
+      if (p.ntw == 2) return launch_nosplit<F, MT, 2>(a, grid, s);
+    }
+    return launch_nosplit<F, MT, 1>(a, grid, s);
   }
   return hipGetLastError();
 }
@@ -496,7 +518,13 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
     p.ntw = 4;
     p.nwaves = 4;
   } else {
-    p.ntw = 1;
+    // two row blocks (33..64 rows): 32 columns per workgroup when that still
+    // gives 256 workgroups, so that a CU reads one 32-row activation block
+    // (192 KiB at K = 3072) rather than two workgroups' worth; measured at
+    // N = 4096, K = 3072, M = 64: 11.1-12.2 -> 8.6-9.8 us for every format.
+    // (With one row block, 32-column tiles leave half the CUs idle: 1.3-1.8 us
+    // slower at M = 16 and 32.)
+    p.ntw = (p.gz == 2 && ((N + 31) / 32) * p.gz >= 256) ? 2 : 1;
     p.nwaves = 12;
   }
   p.spw = spw_of(kfmt, p.cfg);
