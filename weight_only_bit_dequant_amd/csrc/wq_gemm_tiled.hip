@@ -59,8 +59,10 @@ constexpr int tile_smem() {
 
 // Decode one 16-byte packed chunk of a weight column into operand bytes in
 // LDS: `row` is the column's LDS row, k0 the index of its first 16-byte output
-// chunk in that row (`sc` holds the chunk's scale codes).
-template <int F>
+// chunk in that row (`sc` holds the chunk's scale codes).  SEQ stores each
+// NVFP4 chunk before decoding the next, which bounds the fp32 temporaries
+// where registers are scarce.
+template <int F, bool SEQ = false>
 __device__ __forceinline__ void decode_store(unsigned char* row, int r, int k0, u32x4 w, uint32_t sc) {
   using TF = TileFmt<F>;
   auto at = [&](int p) { return reinterpret_cast<bf16x8*>(row + TF::pos(r, k0 + p) * 16); };
@@ -86,7 +88,10 @@ __device__ __forceinline__ void decode_store(unsigned char* row, int r, int k0, 
   } else if constexpr (F == KF_NVFP4) {
     const float d0 = e4m3_decode(sc & 0xFFu), d1 = e4m3_decode((sc >> 8) & 0xFFu);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *at(j) = dec_fp4_mul(w[j], j < 2 ? d0 : d1);
+    for (int j = 0; j < 4; ++j) {
+      *at(j) = dec_fp4_mul(w[j], j < 2 ? d0 : d1);
+      if constexpr (SEQ) __builtin_amdgcn_sched_barrier(0);
+    }
   } else if constexpr (F == KF_MXFP4) {
     const float p = e8m0_decode(sc);
 #pragma unroll
@@ -416,7 +421,10 @@ __global__ __launch_bounds__(NW * 64) void k_woq_gemm256(LinearArgs a) {
     for (int q = 0; q < NB; ++q) {
       const int id = (q * NT + tid) % CB;
       const int col = id / LB, part = id % LB;
-      decode_store<F>(B + col * 128, col, part * (DB / 16), w[q], sc[q]);
+      // (NVFP4: chunk by chunk; decoded all at once, its fp32 temporaries
+      // pushed the kernel past 256 registers and spilled, 145 against 116 us
+      // at M = N = 4096, K = 3072)
+      decode_store<F, true>(B + col * 128, col, part * (DB / 16), w[q], sc[q]);
     }
   };
 
