@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void k_mx_quant_act(const uint16_t* __restrict
 // through LDS as in the bf16 kernel.
 template <int MT>
 __global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
-  constexpr int NW = 12, SPW = 2, NT = 16, NTHR = NW * 64;
+  constexpr int NW = 12, SPW = 2, NT = 16;
   constexpr int E = MT * 16 * NT;
   __shared__ __attribute__((aligned(16))) float red[NW * E];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
