@@ -1,0 +1,69 @@
+"""GPU parity over a seeded sweep of Linear shapes, one format each, chosen so
+that every launch configuration of the dequant-GEMM is hit with ragged edges:
+the one/two-row kernel, the 16- and 32-row no-split kernels (16- and
+32-column tiles), the split-K path with its reduction kernel, and the tiled
+kernels (64x64 with two or four K groups, 128x64, 64x128, 128x128).  Outputs
+are compared with the oracle's fp64 result on the dequantized weight at the
+same bar as the other parity tests (relative Frobenius error 1e-2)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codecs as C
+from oracle import gemm as G
+from oracle import quant as Q
+from weight_only_bit_dequant_amd import synth
+
+wq = pytest.importorskip("weight_only_bit_dequant_amd.wq")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REL_TOL = 1e-2
+FMTS = ["int4", "fp8", "nvfp4", "mxfp4", "int4_asym"]
+# (M range, N range, K range) per regime; N and K are rounded to each format's
+# block below
+REGIMES = [
+    ((1, 2), (2048, 4160), (256, 3072)),      # one/two rows, direct operand loads
+    ((3, 16), (2048, 4160), (256, 3072)),     # 16-row no-split
+    ((17, 32), (2048, 4160), (256, 3072)),    # 32-row no-split
+    ((33, 64), (4096, 4416), (256, 2048)),    # two row blocks, 32-column tiles
+    ((33, 64), (1024, 2048), (256, 2048)),    # two row blocks, 16-column tiles
+    ((1, 64), (32, 640), (256, 4096)),        # split K across workgroups
+    ((65, 256), (256, 2048), (1024, 3072)),   # 64x64 tiles with K groups
+    ((65, 200), (64, 512), (128, 896)),       # 64x64 tiles, one group
+    ((900, 1100), (1536, 2600), (256, 1280)),  # 128x64 tiles
+    ((1500, 2100), (2048, 3000), (128, 512)),  # 128x128 tiles
+]
+CASES = []
+_rng = np.random.RandomState(20261203)
+for _i, (_mr, _nr, _kr) in enumerate(REGIMES):
+    for _j in range(3):
+        _fmt = FMTS[(3 * _i + _j) % len(FMTS)]
+        CASES.append((_fmt, int(_rng.randint(_mr[0], _mr[1] + 1)), int(_rng.randint(_nr[0], _nr[1] + 1)),
+                      int(_rng.randint(_kr[0], _kr[1] + 1)), 600 + 3 * _i + _j))
+
+
+def _round(fmt, N, K):
+    nb = {"int4": 1, "int4_asym": 1, "fp8": 1, "nvfp4": 16, "mxfp4": 32}[fmt]
+    kb = {"int4": 128, "int4_asym": 128, "fp8": 16, "nvfp4": 32, "mxfp4": 32}[fmt]
+    return max(nb, N // nb * nb), max(kb, K // kb * kb)
+
+
+@pytest.mark.parametrize("fmt,M,N,K,cfg", CASES)
+def test_linear_shape_sweep(fmt, M, N, K, cfg):
+    N, K = _round(fmt, N, K)
+    W, b, X = synth.linear_case(N, K, M, cfg=cfg, bias=(cfg % 2 == 0))
+    print(f"[case] sweep fmt={fmt} M={M} N={N} K={K} bias={b is not None}", flush=True)
+    q = wq.quantize(fmt, synth.as_torch_bf16(W, DEV))
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wq.linear(synth.as_torch_bf16(X, DEV), q, None if b is None else synth.as_torch_bf16(b, DEV), out=Y)
+    torch.cuda.synchronize()
+    codes, scales, g = Q.quantize(fmt, W)
+    ref = G.linear_fp64(X, Q.dequant(fmt, codes, scales, g), b)
+    y = C.bf16_to_f32(synth.from_torch_bf16(Y)).astype(np.float64)
+    assert np.isfinite(y).all(), "unwritten output"
+    err = G.rel_frobenius(y, ref)
+    print(f"[parity] sweep {fmt} M={M} N={N} K={K}: rel-F {err:.3e}", flush=True)
+    assert err <= REL_TOL
