@@ -495,19 +495,21 @@ __global__ __launch_bounds__(NW * 64) void k_woq_gemm256(LinearArgs a) {
 
   float s1 = 1.0f;
   if constexpr (F == KF_NVFP4) s1 = a.gscale[0];
+  // epilogue through LDS
+  __syncthreads();  // every wave is done with the tile stages
+  unsigned char* et = smem + wave * (WBM * kTileRowBytes);
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + wn * 64 + 16 * t + c;
     const float bias = bitsf(bias_bits[t] << 16), cs = bitsf(cs_bits[t]);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * WBM + 16 * i + 4 * g + r;
         const float y = (F == KF_FP8) ? acc[i][t][r] * cs : acc[i][t][r] * s1;
-        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
+        tile_put(et, 16 * i + 4 * g + r, 16 * t + c, y + bias);
       }
   }
+  tile_store<WBM>(a.Y, M, N, m0 + wm * WBM, n0 + wn * 64, et, lane);
 }
 
 // ---------------------------------------------------------------- MXFP4, 256 x 256 tiles, weights in registers
@@ -638,18 +640,18 @@ __global__ __launch_bounds__(512) void k_mx_wreg(LinearArgs a) {
   // no LDS write may still be in flight when the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
+  // epilogue through LDS
+  __syncthreads();  // every wave is done with the activation stages
+  unsigned char* et = smem + wave * (128 * kTileRowBytes);
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + wn * 64 + 16 * t + c;
     const float bias = bitsf(bias_bits[t] << 16);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 128 + 16 * i + 4 * g + r;
-        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][t][r] + bias);
-      }
+      for (int r = 0; r < 4; ++r) tile_put(et, 16 * i + 4 * g + r, 16 * t + c, acc[i][t][r] + bias);
   }
+  tile_store<128>(a.Y, M, N, m0 + wm * 128, n0 + wn * 64, et, lane);
 }
 
 template <int F, int BM, int BN, int KS, int WGN = 2>
@@ -677,7 +679,7 @@ hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t 
   if constexpr (F == KF_MXFP4) {
     if (p.bm == 256) {
       static std::atomic<int> done{0};
-      constexpr int sm = 2 * 256 * 256;
+      constexpr int sm = (2 * 256 * 256 > 8 * 128 * kTileRowBytes) ? 2 * 256 * 256 : 8 * 128 * kTileRowBytes;
       auto k = k_mx_wreg;
       hipError_t e = allow_smem(k, sm, done);
       if (e != hipSuccess) return e;
@@ -687,7 +689,7 @@ hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t 
   }
   if (p.bm == 256) {
     static std::atomic<int> done{0};
-    constexpr int sm = 2 * 2 * 256 * 128;
+    constexpr int sm = (2 * 2 * 256 * 128 > kWoqWaves * 128 * kTileRowBytes) ? 2 * 2 * 256 * 128 : kWoqWaves * 128 * kTileRowBytes;
     auto k = k_woq_gemm256<F, kWoqWaves>;
     hipError_t e = allow_smem(k, sm, done);
     if (e != hipSuccess) return e;

@@ -412,7 +412,8 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
 // reads its operands and runs its 16 MFMAs.
 constexpr int kF8T = 256;                 // tile rows and columns
 constexpr int kF8Stage = 2 * kF8T * 128;  // one LDS stage: A then B, 128 codes per row
-constexpr int kF8Smem = 2 * kF8Stage + kF8T * 8;  // + the tile's column scales and biases
+constexpr int kF8Colv = (2 * kF8Stage > 16 * 64 * kTileRowBytes) ? 2 * kF8Stage : 16 * 64 * kTileRowBytes;
+constexpr int kF8Smem = kF8Colv + kF8T * 8;  // stages or output tiles, then the column scales and biases
 
 // LDS slot of 16-byte chunk k (0..7) of tile row r.  An operand read has lane
 // (g, c) take chunks 2g and 2g+1 of row c; a ds_read_b128 serves lanes 0-7
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
   issue(0, 0);
   // the tile's column scales and biases wait in LDS for the epilogue (the
   // loop's first barrier publishes them; issued after the first step's loads), which keeps registers free
-  float* colv = reinterpret_cast<float*>(smem + 2 * kF8Stage);  // [0][256] scale, [1][256] bias
+  float* colv = reinterpret_cast<float*>(smem + kF8Colv);  // [0][256] scale, [1][256] bias
   if (tid < kF8T) {
     colv[tid] = bitsf(bload32(Sr, (uint32_t)(n0 + tid) * 4u));
     colv[kF8T + tid] = bitsf(bload16(Br, (uint32_t)(n0 + tid) * 2u) << 16);
@@ -512,18 +513,19 @@ __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
     }
   }
 
+  // epilogue through LDS (no load is in flight: the last step issued none)
+  static_assert(WBM == 64, "64 x 64 wave tiles");
+  __syncthreads();  // every wave is done with the operand stages
+  unsigned char* et = smem + wave * (64 * kTileRowBytes);
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + wn * 64 + 16 * t + c;
     const float cs = colv[wn * 64 + 16 * t + c], bias = colv[kF8T + wn * 64 + 16 * t + c];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * WBM + 16 * i + 4 * g + r;
-        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16((acc[i][t][r] * s1) * cs + bias);
-      }
+      for (int r = 0; r < 4; ++r) tile_put(et, 16 * i + 4 * g + r, 16 * t + c, (acc[i][t][r] * s1) * cs + bias);
   }
+  tile_store<64>(a.Y, M, N, m0 + wm * 64, n0 + wn * 64, et, lane);
 }
 
 // ---------------------------------------------------------------- MXFP4 x MXFP4, 256 x 256 tiles
@@ -547,7 +549,8 @@ __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
 constexpr int kMxT = 256;
 constexpr int kMxCodes = kMxT * 128;                  // one operand's codes per step
 constexpr int kMxStage = 2 * kMxCodes + 2 * kMxT * 8;  // codes, then scales
-constexpr int kMxSmem = 2 * kMxStage + kMxT * 4;  // + the tile's biases
+constexpr int kMxColb = (2 * kMxStage > 16 * 64 * kTileRowBytes) ? 2 * kMxStage : 16 * 64 * kTileRowBytes;
+constexpr int kMxSmem = kMxColb + kMxT * 4;  // stages or output tiles, then the tile's biases
 
 __global__ __launch_bounds__(1024) void k_mx_gemm256(LinearArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(1024) void k_mx_gemm256(LinearArgs a) {
   issue(0, 0);
   // the tile's biases wait in LDS for the epilogue (the loop's first barrier
   // publishes them), which keeps registers free
-  float* colb = reinterpret_cast<float*>(smem + 2 * kMxStage);
+  float* colb = reinterpret_cast<float*>(smem + kMxColb);
   if (tid < kMxT) colb[tid] = bitsf(bload16(Br, (uint32_t)(n0 + tid) * 2u) << 16);
   for (int kt = 0; kt < KT; ++kt) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of step kt are in LDS
@@ -650,18 +653,18 @@ __global__ __launch_bounds__(1024) void k_mx_gemm256(LinearArgs a) {
     }
   }
 
+  // epilogue through LDS (no load is in flight: the last step issued none)
+  __syncthreads();  // every wave is done with the operand stages
+  unsigned char* et = smem + wave * (64 * kTileRowBytes);
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + wn * 64 + 32 * t + c;
     const float bias = colb[wn * 64 + 32 * t + c];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][t][r] + bias);
-      }
+      for (int r = 0; r < 16; ++r) tile_put(et, 32 * i + 8 * (r >> 2) + 4 * g + (r & 3), 32 * t + c, acc[i][t][r] + bias);
   }
+  tile_store<64>(a.Y, M, N, m0 + wm * 64, n0 + wn * 64, et, lane);
 }
 
 template <int BM, int BN, int WGN = 2>
