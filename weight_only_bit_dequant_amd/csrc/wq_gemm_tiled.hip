@@ -315,25 +315,45 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   }
 
   // ---- epilogue: lane holds D[4g + r][c] of every 16x16 tile; the column
-  // operands were fetched before the main loop
+  // operands were fetched before the main loop.  The output tile leaves
+  // through LDS past the group partials (idle: the loop's last barrier is
+  // behind every wave, and only group 0, each wave in its own region, is
+  // left).  Measured at N = 4096, K = 3072, M = 128-1024: 0.3-1.3 us faster
+  // for the 4-bit formats; FP8 on 128 x 128 tiles was 1-2 us slower and keeps
+  // the element stores.
   float s1 = 1.0f;
   if constexpr (F == KF_NVFP4) s1 = a.gscale[0];
+  if constexpr (F == KF_FP8 || F == KF_BF16) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int n = n0 + wn * WBN + 16 * t + c;
+      const float bias = bitsf(bias_bits[t] << 16);
+      const float cs = bitsf(cs_bits[t]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
+          const float y = (F == KF_FP8) ? acc[i][t][r] * cs : acc[i][t][r];
+          if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
+        }
+    }
+    return;
+  }
+  constexpr int EOFF = (KS - 1) * BM * BN * 4;
+  static_assert(EOFF + 2 * WGN * (BM / 2) * kTileRowBytes <= KS * tile_smem<F, BM, BN>(), "output tiles fit in LDS");
+  unsigned char* et = smem + EOFF + wave * ((BM / 2) * kTileRowBytes);
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + wn * WBN + 16 * t + c;
     const float bias = bitsf(bias_bits[t] << 16);
-    const float cs = bitsf(cs_bits[t]);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * (BM / 2) + 16 * i + 4 * g + r;
-        float y;
-        if constexpr (F == KF_FP8) y = acc[i][t][r] * cs;
-        else y = acc[i][t][r] * s1;
-        if (m < M && n < N) a.Y[(int64_t)m * N + n] = f32_to_bf16(y + bias);
+        tile_put(et, 16 * i + 4 * g + r, 16 * t + c, acc[i][t][r] * s1 + bias);
       }
   }
+  tile_store<BM / 2, WBN>(a.Y, M, N, m0 + wm * (BM / 2), n0 + wn * WBN, et, lane);
 }
 
 // ---------------------------------------------------------------- 256 x 256 tiles

@@ -184,27 +184,31 @@ struct Epilogue {
   }
 };
 
-// Output tiles of the large GEMMs leave through LDS: a wave writes its ROWS x
-// 64 bf16 tile in row-major order (rows padded to kTileRowBytes: the four row
-// groups 4g + r of a 16 x 16 result, or the two of a 32 x 32 one, land 64
-// bytes apart in the banks), then stores it as 16-byte row pieces, 8 rows of
-// 128 bytes per store instruction, instead of one 2-byte store per element.
-// Measured on the static FP8 GEMM at M = N = 4096, K = 3072: 49.8 -> 47.2 us.
+// Output tiles of the tiled GEMMs leave through LDS: a wave writes its ROWS x
+// COLS (COLS = 32 or 64) bf16 tile in row-major order (rows padded to
+// kTileRowBytes: the four row groups 4g + r of a 16 x 16 result, or the two of
+// a 32 x 32 one, land 64 bytes apart in the banks), then stores it as 16-byte
+// row pieces, 64 lanes x 16 bytes per store instruction, instead of one
+// 2-byte store per element.  Measured on the static FP8 GEMM at
+// M = N = 4096, K = 3072: 49.8 -> 47.2 us.
 constexpr int kTileRowBytes = 64 * 2 + 16;
 
 __device__ __forceinline__ void tile_put(unsigned char* et, int row, int col, float y) {
   *reinterpret_cast<uint16_t*>(et + row * kTileRowBytes + col * 2) = f32_to_bf16(y);
 }
 
-// Rows mw .. mw+ROWS-1, columns nw .. nw+63 of Y from the wave's LDS tile;
-// whole tiles with N % 8 == 0 take 16-byte stores (the ABI's 16-byte aligned
-// Y makes them aligned), edge tiles store the elements inside M x N.
-template <int ROWS>
+// Rows mw .. mw+ROWS-1, columns nw .. nw+COLS-1 of Y from the wave's LDS
+// tile; whole tiles with N % 8 == 0 take 16-byte stores (the ABI's 16-byte
+// aligned Y makes them aligned), edge tiles store the elements inside M x N.
+template <int ROWS, int COLS = 64>
 __device__ __forceinline__ void tile_store(uint16_t* Y, int M, int N, int mw, int nw, const unsigned char* et, int lane) {
-  const bool full = mw + ROWS <= M && nw + 64 <= N && (N & 7) == 0;
+  static_assert(COLS == 32 || COLS == 64, "32 or 64 columns");
+  constexpr int LPR = COLS / 8, RPI = 64 / LPR;  // lanes per row, rows per instruction
+  static_assert(ROWS % RPI == 0, "whole store instructions");
+  const bool full = mw + ROWS <= M && nw + COLS <= N && (N & 7) == 0;
 #pragma unroll
-  for (int q = 0; q < ROWS / 8; ++q) {
-    const int row = 8 * q + (lane >> 3), col = 8 * (lane & 7);
+  for (int q = 0; q < ROWS / RPI; ++q) {
+    const int row = RPI * q + lane / LPR, col = 8 * (lane % LPR);
     const u32x4 v = *reinterpret_cast<const u32x4*>(et + row * kTileRowBytes + col * 2);
     const int m = mw + row, n = nw + col;
     if (full) {
