@@ -212,7 +212,9 @@ __device__ __forceinline__ void tile_store(uint16_t* Y, int M, int N, int mw, in
     const u32x4 v = *reinterpret_cast<const u32x4*>(et + row * kTileRowBytes + col * 2);
     const int m = mw + row, n = nw + col;
     if (full) {
-      *reinterpret_cast<u32x4*>(Y + (int64_t)m * N + n) = v;
+      // non-temporal: the output is not read again by this kernel (MXFP4 at
+      // M = N = 4096, K = 3072: 97-99 -> 93 us)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(Y + (int64_t)m * N + n));
     } else if (m < M) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
