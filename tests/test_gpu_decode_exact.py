@@ -1,0 +1,46 @@
+"""Every dequant-GEMM kernel's in-register decode, pinned element by element:
+with an identity block as the activations (X[m][k] = 1 where k = m, else 0)
+and no bias, output row m is the dequantized weight column m, which the GEMM
+must reproduce bit for bit as the bf16 dequantized weight of the oracle
+(every format's decode is exact before that one rounding; INT4's group sum
+reduces to s * code exactly).  A -0 weight comes out as +0, since the sums
+start from +0.  Shapes reach the one/two-row kernel, the
+16- and 32-row kernels, the split-K path and the tiled kernels (one and
+several K groups, and the 256 x 256 kernels)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant as Q
+from weight_only_bit_dequant_amd import synth
+
+wq = pytest.importorskip("weight_only_bit_dequant_amd.wq")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+FMTS = ["int4", "fp8", "nvfp4", "mxfp4", "int4_asym"]
+# (M, N, K): M rows of the identity; the kernel is chosen by M and N
+SHAPES = [(2, 4096, 256), (16, 4096, 256), (32, 4096, 384), (48, 4096, 256), (32, 256, 1024), (128, 512, 256),
+          (128, 1024, 1024), (256, 4096, 512), (4096, 3072, 4096)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_decode_through_gemm_exact(fmt, M, N, K):
+    W = synth.linear_weight(N, K, synth.SEED_W + 90 + M)
+    codes, scales, g = Q.quantize(fmt, W)
+    want = Q.dequant_bf16(fmt, codes, scales, g)[:, :M].T.copy()  # [M][N]
+    want[want == 0x8000] = 0  # a -0 weight gives +0: the sum starts from +0
+    X = np.zeros((M, K), dtype=np.uint16)
+    X[np.arange(M), np.arange(M)] = 0x3F80  # bf16 1.0
+    print(f"[case] decode {fmt} M={M} N={N} K={K}", flush=True)
+    q = wq.quantize(fmt, synth.as_torch_bf16(W, DEV))
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(max(1, wq.wq_linear_workspace(fmt, M, N, K)), dtype=torch.uint8, device=DEV)
+    wq.wq_linear(fmt, synth.as_torch_bf16(X, DEV), q["packed"], q["scales"], q["global"], None, N, Y, ws)
+    torch.cuda.synchronize()
+    got = synth.from_torch_bf16(Y)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:3].tolist()}"
