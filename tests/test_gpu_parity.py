@@ -146,6 +146,16 @@ def test_linear_two_row_blocks_wide(fmt, N, M):
     assert_close(Y, oracle_linear(fmt, W, b, X), f"{fmt} M={M} N={N}")
 
 
+@pytest.mark.parametrize("fmt,N", [("int4", 4100), ("fp8", 4100), ("nvfp4", 4112), ("mxfp4", 4128), ("int4_asym", 4100)])
+@pytest.mark.parametrize("M", [65, 100, 128])
+def test_linear_wide_64_column_tiles(fmt, N, M):
+    # 65..128 rows on a wide layer: three or four row blocks of 64-column
+    # workgroups of 8 waves, with a column tail inside the last tile
+    W, b, X = synth.linear_case(N, 768, M, cfg=40 + M)
+    _, Y = run_linear(fmt, W, b, X)
+    assert_close(Y, oracle_linear(fmt, W, b, X), f"{fmt} M={M} N={N}")
+
+
 @pytest.mark.parametrize("fmt,N", [("int4", 200), ("fp8", 200), ("nvfp4", 208), ("mxfp4", 224), ("int4_asym", 200)])
 def test_linear_ragged_n(fmt, N):
     # column tail that does not fill the 64-column workgroup tile

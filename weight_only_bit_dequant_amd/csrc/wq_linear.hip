@@ -1,4 +1,5 @@
-// Dequant-GEMM for small M (M <= 64): Y = X . deq(W)^T (+ b).
+// Dequant-GEMM for small M (M <= 64, and up to 128 on wide layers):
+// Y = X . deq(W)^T (+ b).
 //
 // Every weight-only page's intro describes the engine it wants: the weight stays
 // packed in device memory and a dequantization prologue feeds a high-precision
@@ -408,15 +409,18 @@ constexpr int spw_split() {
   return (F == KF_BF16) ? 4 : ((F == KF_FP8 || F == KF_FP8S) ? 2 : 1);
 }
 
+// 64-column tiles (NTW = 4) run 8 waves of 1.5x the K: at 12 waves their
+// loads and accumulators spilled registers.
 template <int F, int MT, int NTW>
 hipError_t launch_nosplit(const LinearArgs& a, dim3 grid, hipStream_t s) {
-  constexpr int sm = smem_bytes<F, MT, NTW, 12>(true);
+  constexpr int NW = (NTW == 4) ? 8 : 12;
+  constexpr int sm = smem_bytes<F, MT, NTW, NW>(true);
   static_assert(sm <= 160 * 1024, "no-split tile exceeds the LDS of a CU");
   static std::atomic<int> done{0};
-  auto k = k_linear<F, MT, NTW, 12, spw_nosplit<F>(), true>;
+  auto k = k_linear<F, MT, NTW, NW, spw_nosplit<F>() * 12 / NW, true>;
   hipError_t e = allow_smem(k, sm, done);
   if (e != hipSuccess) return e;
-  k<<<grid, 768, sm, s>>>(a, 1);
+  k<<<grid, NW * 64, sm, s>>>(a, 1);
   return hipGetLastError();
 }
 
@@ -445,6 +449,9 @@ hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
     // no-split tiles with activations staged through LDS
     if constexpr (MT == 2) {
       if (p.ntw == 2) return launch_nosplit<F, MT, 2>(a, grid, s);
+    if constexpr (MT == 2 && F != KF_BF16 && F != KF_FP8S) {
+      if (p.ntw == 4) return launch_nosplit<F, MT, 4>(a, grid, s);
+    }
     }
     return launch_nosplit<F, MT, 1>(a, grid, s);
   }
@@ -475,7 +482,15 @@ int spw_of(int kfmt, int cfg) {
 
 LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
   LinearPlan p{};
-  if (M > 64) {
+  // 65..128 rows of a wide layer (weight-only formats): three or four row
+  // blocks of 64-column tiles (at least 192 workgroups) load everything up
+  // front like the smaller M do, instead of stepping K through LDS tiles.
+  // Measured at N = 4096, K = 3072, M = 72 / 96 / 128: INT4 18.1 -> 12.5 /
+  // 12.6 / 13.2 us, NVFP4 18.4 -> 13.5 / 13.6 / 14.0, MXFP4 15.6 -> 12.3 /
+  // 12.4 / 12.7, FP8 13.9 -> 13.0 / 13.2 / 13.4.
+  const bool wide64 = M > 64 && M <= 128 && kfmt != KF_BF16 && kfmt != KF_FP8S &&
+                      ((N + 63) / 64) * ((M + 31) / 32) >= 192;
+  if (M > 64 && !wide64) {
     // MFMA-bound: LDS-tiled GEMM; the largest tile that still gives about
     // 192 workgroups.  (The static FP8 GEMM's tiled kernels choose their own
     // tiles by the same rule; for it only cfg and the zero workspace matter.)
@@ -511,7 +526,7 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
     return p;
   }
   // 16 or 32 rows per workgroup; 33..64 rows take two row blocks (grid z)
-  // that read the same packed columns.  Workgroup ids of one column tile
+  // that read the same packed columns, 65..128 three or four.  Workgroup ids of one column tile
   // differ by gx, so with gx a multiple of 8 both blocks run on the same XCD
   // (workgroups are dealt to the 8 XCDs round robin) and share its L2 copy.
   p.mt = M <= 16 ? 1 : 2;
@@ -533,9 +548,10 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
     // (With one row block, 32-column tiles leave half the CUs idle: 1.3-1.8 us
     // slower at M = 16 and 32.)
     p.ntw = (p.gz == 2 && ((N + 31) / 32) * p.gz >= 256) ? 2 : 1;
-    p.nwaves = 12;
+    if (p.gz >= 3) p.ntw = 4;  // wide64 above
+    p.nwaves = (p.ntw == 4) ? 8 : 12;
   }
-  p.spw = spw_of(kfmt, p.cfg);
+  p.spw = (p.cfg == kCfgNoSplit) ? spw_of(kfmt, p.cfg) * 12 / p.nwaves : spw_of(kfmt, p.cfg);
   p.gx = (int)((N + 16 * p.ntw - 1) / (16 * p.ntw));
   const int64_t base = (int64_t)p.gx * p.gz;
   int64_t S = 1;
