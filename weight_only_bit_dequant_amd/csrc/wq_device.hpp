@@ -114,6 +114,22 @@ __device__ __forceinline__ float e8m0_decode(uint32_t c) {
 
 __device__ __forceinline__ float clampf(float x, float lo, float hi) { return fminf(fmaxf(x, lo), hi); }
 
+// Static FP8 activation Q ("TorchAO Static FP8 Quantization (Linear)": the
+// calibrated per-tensor scale divides x, the quotient is clamped to the E4M3
+// range and rounded to nearest even): the value before rounding, x itself when
+// s == 0.  One IEEE fp32 division, as in every kernel that applies this Q.
+__device__ __forceinline__ float act_q_val(float x, float s) {
+  return clampf((s > 0.f) ? x / s : x, -448.f, 448.f);
+}
+__device__ __forceinline__ uint32_t act_q(float x, float s) { return e4m3_cvt(act_q_val(x, s)); }
+// eight bf16 values (four words, K order) -> eight E4M3 codes, value i in byte i
+__device__ __forceinline__ u32x2 act_q8(u32x4 v, float s) {
+  return u32x2{e4m3_pack4(act_q_val(bitsf(v.x << 16), s), act_q_val(bitsf(v.x & 0xFFFF0000u), s),
+                          act_q_val(bitsf(v.y << 16), s), act_q_val(bitsf(v.y & 0xFFFF0000u), s)),
+               e4m3_pack4(act_q_val(bitsf(v.z << 16), s), act_q_val(bitsf(v.z & 0xFFFF0000u), s),
+                          act_q_val(bitsf(v.w << 16), s), act_q_val(bitsf(v.w & 0xFFFF0000u), s))};
+}
+
 // Nonnegative float atomic max via the ordered integer view (valid for x >= 0, not NaN).
 __device__ __forceinline__ void atomic_max_nonneg(float* p, float x) {
   atomicMax(reinterpret_cast<unsigned int*>(p), fbits(x));

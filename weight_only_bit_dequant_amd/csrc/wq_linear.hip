@@ -10,9 +10,9 @@
 //    columns (32 for two row blocks) x all of K; each wave owns a contiguous
 //    K range (split-K inside the workgroup).  Split tiles (narrow layers): 4 waves = 64 columns x a K
 //    range, with the K ranges of one column tile spread over S workgroups;
-//  * each wave issues every load of its K range (activations first, then
-//    packed weights and block scales; bias and column scale at the start)
-//    before the first wait, as buffer loads whose out-of-range offsets read
+//  * each wave issues every load of its K range (activations, packed weights
+//    and block scales; bias and column scale at the start) before the first
+//    wait, as buffer loads whose out-of-range offsets read
 //    zero (no branches around loads);
 //  * activations (M <= 32 rows per workgroup) are loaded with contiguous
 //    16-byte loads into a private LDS slot per wave and read back in the
@@ -151,57 +151,71 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   const int wi = (XLDS && S == 1) ? (wave + (int)(blockIdx.x % NW)) % NW : split * NW + wave;
   for (int blk = wi; blk * SPW < T; blk += S * NW) {
     // ---- issue every load of this block before any wait: the activation
-    // slices first (cache hits; loads return in issue order, so their LDS
-    // staging can start while the weight stream is still in flight), then
-    // the packed weights and block scales
+    // slices (cache hits; loads return in issue order, so their LDS staging
+    // can start while the weight stream is still in flight) and the packed
+    // weights and block scales
     u32x4 w[SPW][NTW];
     u32x4 xv[SPW][MT][XL];
     uint32_t sc[SPW][NTW];
+    auto load_x = [&]() {
 #pragma unroll
-    for (int st = 0; st < SPW; ++st) {
-      const int kl = (blk * SPW + st) * MACRO + g * KPL;
-      const bool kv = kl < K;
+      for (int st = 0; st < SPW; ++st) {
+        const int kl = (blk * SPW + st) * MACRO + g * KPL;
+        const bool kv = kl < K;
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const uint32_t m = (uint32_t)(m0 + 16 * i + c);
+        for (int i = 0; i < MT; ++i) {
+          const uint32_t m = (uint32_t)(m0 + 16 * i + c);
 #pragma unroll
-        for (int j = 0; j < XL; ++j) {
-          if constexpr (XLDS) {
-            // contiguous: instruction q covers rows q*R .. q*R+R-1 of the slice
-            const int q = i * XL + j;
-            const uint32_t row = (uint32_t)(m0 + q * XS::R + lane / XS::L);
-            const int kx = (blk * SPW + st) * MACRO + (lane % XS::L) * (16 / XS::XB);
-            xv[st][i][j] = bload128(Xr, off_if(kx < K, (row * (uint32_t)K + (uint32_t)kx) * (uint32_t)XS::XB));
-          } else if constexpr (ACT8) {
-            xv[st][i][j] = bload128(Xr, off_if(kv, m * (uint32_t)K + (uint32_t)kl));
-          } else {
-            xv[st][i][j] = bload128(Xr, off_if(kv, (m * (uint32_t)K + (uint32_t)kl + 8u * j) * 2u));
+          for (int j = 0; j < XL; ++j) {
+            if constexpr (XLDS) {
+              // contiguous: instruction q covers rows q*R .. q*R+R-1 of the slice
+              const int q = i * XL + j;
+              const uint32_t row = (uint32_t)(m0 + q * XS::R + lane / XS::L);
+              const int kx = (blk * SPW + st) * MACRO + (lane % XS::L) * (16 / XS::XB);
+              xv[st][i][j] = bload128(Xr, off_if(kx < K, (row * (uint32_t)K + (uint32_t)kx) * (uint32_t)XS::XB));
+            } else if constexpr (ACT8) {
+              xv[st][i][j] = bload128(Xr, off_if(kv, m * (uint32_t)K + (uint32_t)kl));
+            } else {
+              xv[st][i][j] = bload128(Xr, off_if(kv, (m * (uint32_t)K + (uint32_t)kl + 8u * j) * 2u));
+            }
           }
         }
       }
-    }
+    };
+    auto load_w = [&]() {
 #pragma unroll
-    for (int st = 0; st < SPW; ++st) {
-      const int kl = (blk * SPW + st) * MACRO + g * KPL;
-      const bool kv = kl < K;
+      for (int st = 0; st < SPW; ++st) {
+        const int kl = (blk * SPW + st) * MACRO + g * KPL;
+        const bool kv = kl < K;
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const uint32_t n = (uint32_t)(n0 + 16 * t + c);
-        // 4-bit weights stream past the caches (non-temporal), which keeps
-        // the activations, read by every workgroup, resident: measured at
-        // N = 4096, K = 3072, M = 32: INT4 6.7 -> 6.55 us, NVFP4 7.4 -> 7.2,
-        // MXFP4 6.8 -> 6.7; FP8 gained nothing at M = 32 and lost 0.3 us at
-        // M = 1
-        if constexpr (F == KF_INT4 || F == KF_INT4A || F == KF_NVFP4 || F == KF_MXFP4)
-          w[st][t] = bload128_nt(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
-        else
-          w[st][t] = bload128(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
-        if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u));
-        else if constexpr (F == KF_INT4A) sc[st][t] = bload32(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 4u));
-        else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, off_if(kv, n * (uint32_t)(K / 16) + (uint32_t)(kl / 16)));
-        else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, off_if(kv, n * (uint32_t)(K / 32) + (uint32_t)(kl / 32)));
-        else sc[st][t] = 0u;
+        for (int t = 0; t < NTW; ++t) {
+          const uint32_t n = (uint32_t)(n0 + 16 * t + c);
+          // 4-bit weights stream past the caches (non-temporal), which keeps
+          // the activations, read by every workgroup, resident: measured at
+          // N = 4096, K = 3072, M = 32: INT4 6.7 -> 6.55 us, NVFP4 7.4 -> 7.2,
+          // MXFP4 6.8 -> 6.7; FP8 gained nothing at M = 32 and lost 0.3 us at
+          // M = 1
+          if constexpr (F == KF_INT4 || F == KF_INT4A || F == KF_NVFP4 || F == KF_MXFP4)
+            w[st][t] = bload128_nt(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
+          else
+            w[st][t] = bload128(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
+          if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u));
+          else if constexpr (F == KF_INT4A) sc[st][t] = bload32(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 4u));
+          else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, off_if(kv, n * (uint32_t)(K / 16) + (uint32_t)(kl / 16)));
+          else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, off_if(kv, n * (uint32_t)(K / 32) + (uint32_t)(kl / 32)));
+          else sc[st][t] = 0u;
+        }
       }
+    };
+    // NVFP4 issues its weights first: measured at N = 4096, K = 3072, M = 32,
+    // 7.3-7.4 -> 7.0-7.1 us (unchanged at M = 4 and 64); FP8 and INT4 were
+    // 0.05-0.25 us slower that way, MXFP4 unchanged.
+    if constexpr (F == KF_NVFP4) {
+      load_w();
+      load_x();
+    } else {
+      load_x();
+      load_w();
     }
     // Keep every load above in flight together: left alone, the scheduler
     // sinks them towards their uses to save registers, which leaves only 6-10
@@ -453,9 +467,9 @@ hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
     // no-split tiles with activations staged through LDS
     if constexpr (MT == 2) {
       if (p.ntw == 2) return launch_nosplit<F, MT, 2>(a, grid, s);
-    if constexpr (MT == 2 && F != KF_BF16 && F != KF_FP8S) {
-      if (p.ntw == 4) return launch_nosplit<F, MT, 4>(a, grid, s);
-    }
+      if constexpr (F != KF_BF16 && F != KF_FP8S) {
+        if (p.ntw == 4) return launch_nosplit<F, MT, 4>(a, grid, s);
+      }
     }
     return launch_nosplit<F, MT, 1>(a, grid, s);
   }

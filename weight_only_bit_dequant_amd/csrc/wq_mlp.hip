@@ -25,20 +25,6 @@ namespace wq {
 
 namespace {
 
-// The static activation Q before rounding: clamp(x / s, +-448) (x itself when
-// s == 0); e4m3_cvt / e4m3_pack4 round it to E4M3.
-__device__ __forceinline__ float q_val(float x, float s) {
-  return clampf((s > 0.f) ? x / s : x, -448.f, 448.f);
-}
-__device__ __forceinline__ uint32_t q_act(float x, float s) { return e4m3_cvt(q_val(x, s)); }
-// eight bf16 values (four words) -> eight codes
-__device__ __forceinline__ u32x2 q_act8(u32x4 v, float s) {
-  return u32x2{e4m3_pack4(q_val(bitsf(v.x << 16), s), q_val(bitsf(v.x & 0xFFFF0000u), s), q_val(bitsf(v.y << 16), s),
-                          q_val(bitsf(v.y & 0xFFFF0000u), s)),
-               e4m3_pack4(q_val(bitsf(v.z << 16), s), q_val(bitsf(v.z & 0xFFFF0000u), s), q_val(bitsf(v.w << 16), s),
-                          q_val(bitsf(v.w & 0xFFFF0000u), s))};
-}
-
 __device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
@@ -179,7 +165,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_static_mlp2_sp(Mlp2Args a) {
 
   // ---- X -> E4M3 codes; layer-1 weight rows -> the wave's slab
   if (xr < 16) {
-    *reinterpret_cast<u32x2*>(Xq + xr * kSpRS1 + xk) = q_act8(xv, s1);
+    *reinterpret_cast<u32x2*>(Xq + xr * kSpRS1 + xk) = act_q8(xv, s1);
   }
   store_slab(slab, w1, lane);
   __syncthreads();
@@ -198,7 +184,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_static_mlp2_sp(Mlp2Args a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float h = bf16_to_f32(f32_to_bf16((acc[j][r] * s1) * ws + b));
-        Hq[(4 * g + r) * kSpRS2 + n] = n < N1 ? (uint8_t)q_act(h, s2) : (uint8_t)0;
+        Hq[(4 * g + r) * kSpRS2 + n] = n < N1 ? (uint8_t)act_q(h, s2) : (uint8_t)0;
       }
     }
   }
@@ -286,7 +272,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_static_mlp2(Mlp2Args a) {
   for (int i = tid; i < 16 * K1 / 8; i += NTHR) {
     const int r = (i * 8) / K1, k = (i * 8) % K1;
     const u32x4 v = bload128(Xr, ((uint32_t)(m0 + r) * (uint32_t)K1 + (uint32_t)k) * 2u);  // rows past M read 0
-    *reinterpret_cast<u32x2*>(Xq + r * RS1 + k) = q_act8(v, s1);
+    *reinterpret_cast<u32x2*>(Xq + r * RS1 + k) = act_q8(v, s1);
   }
   __syncthreads();
 
@@ -310,7 +296,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_static_mlp2(Mlp2Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float h = bf16_to_f32(f32_to_bf16((acc[j][r] * s1) * E1[n] + E1[N1 + n]));
-          Hq[(4 * g + r) * RS2 + n] = (uint8_t)q_act(h, s2);
+          Hq[(4 * g + r) * RS2 + n] = (uint8_t)act_q(h, s2);
         }
       }
     }

@@ -314,17 +314,6 @@ __global__ void k_fp8_scale(const float* __restrict__ amax, float* __restrict__ 
 // element tail (numel % 8) goes to the thread whose chunk index equals the
 // chunk count.
 constexpr int kQActChunks = 4;
-__device__ __forceinline__ u32x2 quant8(u32x4 v, float s) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float q[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float x = bitsf((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
-    q[i] = clampf((s > 0.f) ? x / s : x, -448.f, 448.f);
-  }
-  return u32x2{e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7])};
-}
-
 __global__ __launch_bounds__(kThreads) void k_quant_act(const uint16_t* __restrict__ X, int64_t numel,
                                                         const float* __restrict__ act_scale,
                                                         uint8_t* __restrict__ Xq) {
@@ -338,17 +327,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(const uint16_t* __restri
 #pragma unroll
     for (int q = 0; q < kQActChunks; ++q) v[q] = X16[c0 + q * kThreads];
 #pragma unroll
-    for (int q = 0; q < kQActChunks; ++q) Q8[c0 + q * kThreads] = quant8(v[q], s);
+    for (int q = 0; q < kQActChunks; ++q) Q8[c0 + q * kThreads] = act_q8(v[q], s);
     return;
   }
   for (int q = 0; q < kQActChunks; ++q) {
     const int64_t c = c0 + q * kThreads;
     if (c < full) {
-      Q8[c] = quant8(X16[c], s);
+      Q8[c] = act_q8(X16[c], s);
     } else if (c == full) {
       for (int64_t i = full * 8; i < numel; ++i) {
         const float x = bf16_to_f32(X[i]);
-        Xq[i] = (uint8_t)e4m3_encode(clampf((s > 0.f) ? x / s : x, -448.f, 448.f));
+        Xq[i] = (uint8_t)e4m3_encode(act_q_val(x, s));
       }
     }
   }
