@@ -280,6 +280,24 @@ def test_static_act_quant_every_bf16(scale):
     assert np.array_equal(host(Xq), S.quantize_act(X, np.float32(scale)))
 
 
+def test_static_act_quant_beyond_one_grid_pass():
+    """An activation tensor with more 8-element chunks than one capped grid
+    covers (2^24 chunks), plus a ragged tail: the threads stride over the
+    rest.  Checked on slices around the first pass's end and at both ends
+    (the Q is elementwise, so the oracle runs on each slice alone)."""
+    n = (1 << 27) + (1 << 20) + 13
+    print(f"[case] static act quant numel={n}", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(404)
+    x = (torch.randn(1, n, generator=gen, device=DEV) * 3.0).to(torch.bfloat16)
+    t_s = torch.tensor([0.0123], dtype=torch.float32, device=DEV)
+    xq = torch.empty((1, n), dtype=torch.uint8, device=DEV)
+    wq.wq_fp8_quantize_act(x, t_s, xq)
+    torch.cuda.synchronize()
+    for a, b in [(0, 1 << 16), ((1 << 27) - (1 << 16), (1 << 27) + (1 << 16)), (n - (1 << 16) - 13, n)]:
+        xs = host_bits(x[:, a:b].contiguous())
+        assert np.array_equal(host(xq[:, a:b]), S.quantize_act(xs, np.float32(0.0123))), (a, b)
+
+
 def _gpu_static_layer(x_dev, act_scale, Wq, w_scale):
     return wq.static_fp8_linear(x_dev, act_scale, Wq, w_scale)
 
