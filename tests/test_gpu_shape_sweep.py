@@ -6,6 +6,8 @@ kernels (64x64 with two or four K groups, 128x64, 64x128, 128x128).  Outputs
 are compared with the oracle's fp64 result on the dequantized weight at the
 same bar as the other parity tests (relative Frobenius error 1e-2)."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -36,13 +38,16 @@ REGIMES = [
     ((900, 1100), (1536, 2600), (256, 1280)),  # 128x64 tiles
     ((1500, 2100), (2048, 3000), (128, 512)),  # 128x128 tiles
 ]
+# WQ_SWEEP_SEED / WQ_SWEEP_PER_REGIME draw a different or larger sweep (the
+# default is the committed one)
 CASES = []
-_rng = np.random.RandomState(20261203)
+_PER = int(os.environ.get("WQ_SWEEP_PER_REGIME", "3"))
+_rng = np.random.RandomState(int(os.environ.get("WQ_SWEEP_SEED", "20261203")))
 for _i, (_mr, _nr, _kr) in enumerate(REGIMES):
-    for _j in range(3):
+    for _j in range(_PER):
         _fmt = FMTS[(3 * _i + _j) % len(FMTS)]
         CASES.append((_fmt, int(_rng.randint(_mr[0], _mr[1] + 1)), int(_rng.randint(_nr[0], _nr[1] + 1)),
-                      int(_rng.randint(_kr[0], _kr[1] + 1)), 600 + 3 * _i + _j))
+                      int(_rng.randint(_kr[0], _kr[1] + 1)), 600 + _PER * _i + _j))
 
 
 def _round(fmt, N, K):
