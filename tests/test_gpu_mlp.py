@@ -1,6 +1,8 @@
 """The fused two-layer static-FP8 MLP (wq_fp8_static_mlp2) against the oracle's
 quantized model and against two unfused wq_fp8_static_linear calls."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -71,3 +73,22 @@ def test_page_mlp():
                                               (16, 272, 256, 64, False), (64, 512, 1024, 100, False)])
 def test_ragged_and_deep(M, K1, N1, N2, bias):
     run_case(M, K1, N1, N2, bias, 710 + M)
+
+
+# seeded sweep over both kernel forms: about a third of the shapes fit the
+# single-pass kernel (K1 <= 256, N1 <= 512, N2 <= 128), the rest loop; M spans
+# one to several row blocks of 16.  WQ_SWEEP_SEED / WQ_SWEEP_PER_REGIME draw
+# another or a larger sweep.
+_PER = int(os.environ.get("WQ_SWEEP_PER_REGIME", "3"))
+_rng = np.random.RandomState(int(os.environ.get("WQ_SWEEP_SEED", "20261205")))
+SWEEP = []
+for _lim in [(256, 512, 128), (1024, 1024, 384), (2048, 2048, 64)]:
+    for _j in range(_PER):
+        SWEEP.append((int(_rng.randint(1, 200)), 16 * int(_rng.randint(1, _lim[0] // 16 + 1)),
+                      16 * int(_rng.randint(1, _lim[1] // 16 + 1)), int(_rng.randint(1, _lim[2] + 1)),
+                      bool(_rng.randint(0, 2))))
+
+
+@pytest.mark.parametrize("M,K1,N1,N2,bias", SWEEP)
+def test_mlp2_sweep(M, K1, N1, N2, bias):
+    run_case(M, K1, N1, N2, bias, 900 + M + K1 + N2)
