@@ -8,6 +8,8 @@ static page's sqnr).  Decoding is exact and accumulation is fp32, so the
 observed error is the final bf16 rounding (~1e-3); the tests also record it.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -110,6 +112,29 @@ def test_quantize_edge_weights(fmt, kind):
     W = synth.special_weight(64, 256, 77, kind)
     q = gpu_quantize(fmt, W)
     check_quant_exact(fmt, W, q)
+
+
+# seeded sweep of quantizer shapes (N and K rounded to each format's rule) and
+# weight kinds; WQ_SWEEP_SEED / WQ_SWEEP_PER_REGIME draw another or a larger one
+_QPER = int(os.environ.get("WQ_SWEEP_PER_REGIME", "2"))
+_qrng = np.random.RandomState(int(os.environ.get("WQ_SWEEP_SEED", "20261206")))
+QSWEEP = [(fmt, int(_qrng.randint(1, 3000)), int(_qrng.randint(1, 4500)),
+           ["normal", "wide", "negzero", "tiny"][int(_qrng.randint(0, 4))], 320 + 10 * i + j)
+          for i, fmt in enumerate(FMTS) for j in range(_QPER)]
+
+
+@pytest.mark.parametrize("fmt,N,K,kind,seed", QSWEEP)
+def test_quantize_sweep_bit_exact(fmt, N, K, kind, seed):
+    nb = {"int4": 1, "int4_asym": 1, "fp8": 1, "nvfp4": 16, "mxfp4": 32}[fmt]
+    kb = {"int4": 128, "int4_asym": 128, "fp8": 16, "nvfp4": 16, "mxfp4": 32}[fmt]
+    N, K = max(nb, N // nb * nb), max(kb, K // kb * kb)
+    print(f"[case] quantize sweep fmt={fmt} N={N} K={K} kind={kind}", flush=True)
+    W = synth.linear_weight(N, K, seed) if kind == "normal" else synth.special_weight(N, K, seed, kind)
+    q = gpu_quantize(fmt, W)
+    codes, scales, g = check_quant_exact(fmt, W, q)
+    out = wq.dequantize(q)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), Q.dequant_bf16(fmt, codes, scales, g))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
