@@ -224,13 +224,12 @@ def test_linear_mxfp4_m_sweep(M):
         assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"mxfp4 M={M} sampled rows")
 
 
-# (M, N, K) -> tiled workgroup shape / K groups chosen by the plan:
-#   64x64 tiles in 2 K groups (34 steps; 33 steps: the second group's range
-#   ends one step early), 64x64 in 2, 128x64 in 2, 64x128 in 2 (ragged N),
-#   ragged M in 2 groups, 256x256 tiles of 8 waves with ragged M and N (MXFP4,
-#   FP8; INT4 and NVFP4 take 128x128 there)
-# the last two take 256 x 256 tiles (ragged M and N tiles; the last with a
-# partial final K step)
+# (M, N, K) -> tile shape / K groups chosen by the plan (64x64 tiles split K
+# over four groups of 2 waves for the 4-bit formats, two groups of 4 for FP8):
+#   64x64 tiles in K groups (34 steps; 33 steps: the last group's range ends
+#   early), 64x64 in K groups, 128x64 in 2 groups, 64x128 in 2 groups (ragged
+#   N), 64x64 with ragged M; the last two take 256x256 tiles in every format
+#   (ragged M and N tiles; the last with a partial final K step)
 TILED_CASES = [(256, 1024, 2176), (256, 1024, 2112), (640, 2048, 1152), (384, 4096, 1024), (6144, 192, 1024),
                (200, 1024, 2048), (3000, 4000, 1024), (2900, 4160, 1120)]
 
