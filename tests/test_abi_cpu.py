@@ -80,10 +80,10 @@ def test_linear_host_validation():
     assert _call_linear(M=0) == wq.OK
     assert _call_linear(N=0) == wq.OK
     # split-K needs a workspace: a narrow layer (256 columns) splits K
-    need = wq.wq_linear_workspace("int4", 32, 256, 3072)
+    need = wq.wq_linear_workspace("int4", 32, 256, 4096)
     assert need > 0
-    assert _call_linear(M=32, K=3072, N=256, ws=None) == wq.EWORKSPACE
-    assert _call_linear(M=32, K=3072, N=256, ws=64, wsb=need - 1) == wq.EWORKSPACE
+    assert _call_linear(M=32, K=4096, N=256, ws=None) == wq.EWORKSPACE
+    assert _call_linear(M=32, K=4096, N=256, ws=64, wsb=need - 1) == wq.EWORKSPACE
     assert b"workspace" in wq.lib().wq_last_error()
 
 
@@ -113,7 +113,7 @@ def test_quantize_pack_dequant_validation():
     assert L.wq_fp8_linear(v(16), 4, 32, None, v(16), v(16), None, 16, v(16), None, 0, None) == wq.EINVAL
     assert L.wq_fp8_linear(v(8), 4, 32, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.EALIGN
     assert L.wq_fp8_linear(v(16), 0, 32, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.OK
-    assert L.wq_fp8_linear(v(16), 32, 3072, v(16), v(16), v(16), None, 256, v(16), None, 0,
+    assert L.wq_fp8_linear(v(16), 32, 4096, v(16), v(16), v(16), None, 256, v(16), None, 0,
                            None) == wq.EWORKSPACE  # narrow layer: split K
     # MXFP4 dynamic-activation path
     assert L.wq_mx_quantize_act(v(16), 4, 48, v(16), v(16), None) == wq.ESHAPE
@@ -154,8 +154,8 @@ def test_workspace_plans_are_consistent():
     gemm = wq.wq_linear_workspace("fp8", M, N, K)
     assert wq.wq_fp8_static_workspace(M, N, K) >= gemm + M * K
     assert wq.wq_fp8_linear_workspace(M, N, K) == 0
-    assert wq.wq_fp8_linear_workspace(32, 256, 3072) > 0
-    assert wq.wq_fp8_static_workspace(32, 256, 3072) >= wq.wq_fp8_linear_workspace(32, 256, 3072) + 32 * 3072
+    assert wq.wq_fp8_linear_workspace(32, 256, 4096) > 0
+    assert wq.wq_fp8_static_workspace(32, 256, 4096) >= wq.wq_fp8_linear_workspace(32, 256, 4096) + 32 * 4096
     # wide layers have enough workgroups without K splits
     assert wq.wq_linear_workspace("mxfp4", 4096, 4096, 3072) == 0
     assert wq.wq_linear_workspace("int4", 32, 4096, 3072) == 0

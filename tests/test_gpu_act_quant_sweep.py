@@ -32,7 +32,7 @@ REGIMES = [
     ((1, 2), (1024, 4160), (128, 3072)),       # one/two rows
     ((3, 32), (2048, 4160), (128, 3072)),      # 16- and 32-row tiles
     ((33, 64), (1024, 4416), (128, 2048)),     # two row blocks
-    ((1, 64), (32, 640), (128, 4096)),         # narrow layers: split K
+    ((1, 64), (32, 640), (3200, 8192)),        # narrow layers: split K (K > 3072)
     ((65, 400), (64, 1024), (128, 1536)),      # 64 x 64 tiles
     ((600, 1200), (1024, 2048), (128, 1024)),  # 128 x 128 tiles
     ((3000, 4200), (4000, 4400), (128, 512)),  # 256 x 256 tiles

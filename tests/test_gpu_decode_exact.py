@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 FMTS = ["int4", "fp8", "nvfp4", "mxfp4", "int4_asym"]
 # (M, N, K): M rows of the identity; the kernel is chosen by M and N
-SHAPES = [(2, 4096, 256), (16, 4096, 256), (32, 4096, 384), (48, 4096, 256), (96, 4096, 256), (32, 256, 1024),
+SHAPES = [(2, 4096, 256), (16, 4096, 256), (32, 4096, 384), (48, 4096, 256), (96, 4096, 256), (32, 256, 4096),
           (128, 512, 256),
           (128, 1024, 1024), (256, 4096, 512), (4096, 3072, 4096)]
 

@@ -463,7 +463,7 @@ def test_read_stream_xor(nbytes):
 def test_workspace_reuse_across_plans():
     """Calls with different launch plans (K split across workgroups or not)
     share one cached workspace and run back to back."""
-    cases = [(32, 4096, 3072), (64, 256, 1024), (16, 1024, 2048), (64, 256, 1024), (32, 4096, 3072)]
+    cases = [(32, 4096, 3072), (64, 256, 4096), (16, 1024, 6144), (64, 256, 4096), (32, 4096, 3072)]
     for i, (M, N, K) in enumerate(cases):
         W, b, X = synth.linear_case(N, K, M, cfg=60 + i)
         _, Y = run_linear("int4", W, b, X)

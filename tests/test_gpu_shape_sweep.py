@@ -32,7 +32,7 @@ REGIMES = [
     ((17, 32), (2048, 4160), (256, 3072)),    # 32-row no-split
     ((33, 64), (4096, 4416), (256, 2048)),    # two row blocks, 32-column tiles
     ((33, 64), (1024, 2048), (256, 2048)),    # two row blocks, 16-column tiles
-    ((1, 64), (32, 640), (256, 4096)),        # split K across workgroups
+    ((1, 64), (32, 640), (3200, 8192)),       # split K across workgroups (K > 3072)
     ((65, 256), (256, 2048), (1024, 3072)),   # 64x64 tiles with K groups
     ((65, 200), (64, 512), (128, 896)),       # 64x64 tiles, one group
     ((900, 1100), (1536, 2600), (256, 1280)),  # 128x64 tiles
