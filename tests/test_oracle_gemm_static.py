@@ -145,3 +145,29 @@ def test_static_two_layer_sqnr_recorded():
     _, outs = S.quant_forward(x, scales, qw)
     v = G.sqnr(C.bf16_to_f32(fp_out), C.bf16_to_f32(outs[-1]))
     assert 20.0 < v < 40.0
+
+
+def test_quant_forward_chains_the_bf16_layer_output():
+    """Hand-worked two-layer forward ("TorchAO Static FP8 Quantization
+    (Linear)", "Define a small two-layer Linear model": layer 2 takes layer 1's
+    bf16 output; "Graph after export": Q then DQ on that input).
+
+    x = [1, 1], act_scale1 = 2^-6 (x / s = 64, code 0x68), W1 = [[1.0, 3 * 2^-9]]
+    (E4M3 0x38, 0x03), w_scale1 = 1: y1 = 1 + 3 * 2^-9 in fp64, whose bf16
+    rounding is 1 + 2^-7.  act_scale2 = fp32(0.9475): the bf16 input gives
+    (1 + 2^-7) / s2 = 1.0636, above the E4M3 midpoint 1.0625, so code 0x39
+    (1.125); the unrounded fp64 y1 would give 1.0616 -> 0x38 (1.0).  W2 = [[1.0]],
+    w_scale2 = 1, so y2 = 1.125 * s2 (1.0 * s2 with the unrounded input)."""
+    s1, s2 = np.float32(2.0 ** -6), np.float32(0.9475)
+    x = _bf([[1.0, 1.0]])
+    q1 = (np.array([[0x38, 0x03]], np.uint8), np.array([1.0], np.float32))
+    q2 = (np.array([[0x38]], np.uint8), np.array([1.0], np.float32))
+    y, outs = S.quant_forward(x, [s1, s2], [q1, q2])
+    assert outs[0].tolist() == [[0x3F81]]  # bf16 1 + 2^-7
+    assert S.quantize_act(outs[0], s2).tolist() == [[0x39]]
+    assert y.tolist() == [[1.125 * float(s2)]]
+    assert outs[1].tolist() == C.f64_to_bf16(np.array([[1.125 * float(s2)]])).tolist()
+    # the case separates the two chainings: the unrounded layer-1 value
+    # quantizes to another code
+    y1 = 1.0 + 3.0 * 2.0 ** -9
+    assert C.e4m3_encode(np.array([np.float32(np.float32(y1) / s2)])).tolist() == [0x38]

@@ -229,3 +229,76 @@ def test_dequant_bf16_definition(fmt):
     # every format: within one bf16 rounding (plus fp32 rounding) of the exact value
     back = C.bf16_to_f32(got).astype(np.float64)
     assert np.all(np.abs(back - exact) <= np.abs(exact) * (2.0 ** -8 + 2.0 ** -23) + 1e-30)
+
+
+# ------------------------------------------------------------------ double rounding of the bf16 dequantize
+
+
+def _rne_bits(v, bits):
+    """Round the positive rational `v` to `bits` significant bits, nearest with
+    ties to even (exact rational arithmetic, no floating point)."""
+    from fractions import Fraction
+
+    e = 0
+    while v >= 2:
+        v /= 2
+        e += 1
+    while v < 1:
+        v *= 2
+        e -= 1
+    scaled = v * (1 << (bits - 1))
+    q, r = divmod(scaled.numerator, scaled.denominator)
+    half = Fraction(r, scaled.denominator)
+    if half > Fraction(1, 2) or (half == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    return Fraction(q, 1 << (bits - 1)) * Fraction(2) ** e
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_dequant_bf16_double_rounding_hand_example(fmt):
+    """The bf16 dequantize rounds the scale product to fp32 first and then to
+    bf16 (the two-kernel form's DQ output, "TorchAO FP8 Weight-Only
+    Quantization (Linear)", intro).  Hand-worked: the exact product is
+    1 + 2^-8 + 2^-25.  Its fp32 rounding is 1 + 2^-8, the midpoint between the
+    bf16 values 1 and 1 + 2^-7, which goes to the even 1.0 (0x3F80); a single
+    rounding of the exact product would give 1 + 2^-7 (0x3F81)."""
+    from fractions import Fraction
+
+    s = np.float32(0.8031250238418579)  # fp32: 6737101 * 2^-23
+    assert Fraction(float(s)) == Fraction(6737101, 1 << 23)
+    exact = Fraction(5, 4) * Fraction(float(s))
+    assert exact == 1 + Fraction(1, 256) + Fraction(1, 1 << 25)
+    double = _rne_bits(_rne_bits(exact, 24), 8)
+    single = _rne_bits(exact, 8)
+    assert double == 1 and single == 1 + Fraction(1, 128)
+    if fmt == "fp8":
+        got = Q.dequant_bf16("fp8", np.array([[0x3A]], np.uint8), np.array([s], np.float32))  # E4M3 1.25
+    else:
+        # E2M1 1.0 (code 2) x E4M3 block scale 1.25 (0x3A) x global s
+        codes = np.full((16, 16), 2, np.uint8)
+        scales = np.full((16, 1), 0x3A, np.uint8)
+        got = Q.dequant_bf16("nvfp4", codes, scales, s)
+    assert np.all(got == 0x3F80), hex(int(got.ravel()[0]))
+
+
+def test_dequant_fp8_row_reconstruction_bound():
+    """Round to nearest on the E4M3 grid: every weight comes back within half a
+    grid step of w / s, times the row scale s (plus the fp32 rounding of the
+    quotient).  The grid step of E4M3 at |q| in [2^e, 2^(e+1)) is 2^(e-3) for
+    e >= -6 and 2^-9 below 2^-6 (OCP E4M3: 3 mantissa bits, bias 7).  A row
+    scale taken from the wrong row, or a division in place of the product,
+    breaks the bound."""
+    W = np.concatenate([synth.linear_weight(48, 256, 31), synth.special_weight(16, 256, 32, "wide")])
+    codes, s = Q.quantize_fp8_row(W)
+    w = C.bf16_to_f32(W).astype(np.float64)
+    sd = s.astype(np.float64)[:, None]
+
+    def bound_ok(deq):
+        t = np.abs(w) / sd
+        _, ex = np.frexp(np.maximum(t, 2.0 ** -7))
+        step = np.where(t < 2.0 ** -6, 2.0 ** -9, np.exp2(ex - 1 - 3))
+        return np.all(np.abs(w - deq) <= sd * (0.5 * step + 2.0 ** -23 * t) + 1e-300)
+
+    assert bound_ok(Q.dequant_fp8_row(codes, s))
+    assert not bound_ok(Q.dequant_fp8_row(codes, np.roll(s, 1)))
+    assert not bound_ok(C.e4m3_decode(codes) / sd)
