@@ -49,6 +49,29 @@
  *            clamp(rint(w / s) + z, 0, 15); value (code - z) * s.
  * Packing: byte j of a packed row holds element 2j in its low nibble and
  * element 2j+1 in its high nibble.
+ *
+ * Weight layouts (the `layout` argument of the calls that read a packed weight):
+ *   WQ_LAYOUT_ROWS  (0) canonical: packed row n at n * row_bytes (row_bytes =
+ *                   K/2 for 4-bit formats, K for FP8), scales row-major as
+ *                   listed above.  These are the bytes wq_pack writes.
+ *   WQ_LAYOUT_TILES (1) kernel tile order ("TorchAO INT4 Weight-Only
+ *                   Quantization (Linear)", "Export and compile": the packed
+ *                   constant is re-laid-out once for the engine): the packed
+ *                   weight is cut into tiles of 16 rows x 64 bytes (128 K of a
+ *                   4-bit format, 64 K of E4M3); tile (n / 16, b / 64) starts
+ *                   at ((n / 16) * (row_bytes / 64) + b / 64) * 1024 and holds
+ *                   its 16 rows' 64 bytes one after the other, so byte b of row
+ *                   n is at that start + 64 * (n % 16) + b % 64.  Block scales
+ *                   follow the same tiles: for tile (n / 16, j), the 16 rows'
+ *                   scale bytes of K range [128 j, 128 j + 128) one after the
+ *                   other -- INT4 2, INT4_ASYM 4, NVFP4 8, MXFP4 4 bytes per row
+ *                   -- starting at ((n / 16) * (K / 128) + j) * 16 * that size.
+ *                   FP8 row scales and the NVFP4 global scale are the same in
+ *                   both layouts.  Sizes are those of WQ_LAYOUT_ROWS.  Needs
+ *                   N % 16 == 0 and K % 128 == 0 (4-bit) or K % 64 == 0 (FP8)
+ *                   (WQ_EUNSUPPORTED otherwise); BF16 has only layout 0.  One
+ *                   16-byte load per lane of a 64-lane wave then reads a whole
+ *                   tile (8 full cache lines) instead of 16 half lines.
  */
 #ifndef WQ_H
 #define WQ_H
@@ -60,7 +83,7 @@
 extern "C" {
 #endif
 
-#define WQ_ABI_VERSION 1
+#define WQ_ABI_VERSION 2
 
 typedef enum wq_format {
   WQ_BF16 = 0,
@@ -70,6 +93,8 @@ typedef enum wq_format {
   WQ_MXFP4 = 4,
   WQ_INT4_ASYM = 5
 } wq_format;
+
+typedef enum wq_layout_kind { WQ_LAYOUT_ROWS = 0, WQ_LAYOUT_TILES = 1 } wq_layout_kind;
 
 typedef enum wq_status {
   WQ_OK = 0,
@@ -129,7 +154,7 @@ wq_status wq_quantize(int fmt, const void* W, int64_t N, int64_t K, void* codes,
                       float* global_scale, void* stream);
 
 /*
- * Pack unpacked codes into the byte stream wq_linear reads
+ * Pack unpacked codes into the canonical byte stream (WQ_LAYOUT_ROWS)
  * ("TorchAO INT4 Weight-Only Quantization (Linear)", "Export and compile":
  * one-code-per-byte int8 data re-packed into a 4-bit constant).  4-bit formats:
  * two codes per byte, low nibble = even element; FP8: a plain copy.
@@ -138,12 +163,24 @@ wq_status wq_quantize(int fmt, const void* W, int64_t N, int64_t K, void* codes,
 wq_status wq_pack(int fmt, const void* codes, int64_t N, int64_t K, void* packed, void* stream);
 
 /*
- * Dequantize packed weights to bf16 W_out[N][K] (the DQ of the two-kernel form,
- * "TorchAO FP8 Weight-Only Quantization (Linear)", intro).  Each element is
- * bf16(fp32 product) of the code's value and its scale(s), evaluated in the
- * order code * block-scale * global-scale.
+ * Convert a packed weight and its block scales from layout `src_layout` to
+ * `dst_layout` (see "Weight layouts" above; the same page and section as
+ * wq_pack: the one-time re-layout of the packed constant).  src and dst are
+ * distinct buffers of the sizes wq_layout reports.  FP8 row scales are copied
+ * unchanged; the NVFP4 global scale is not touched (it is the same in both
+ * layouts).  Converting back reproduces the source bytes exactly.  Both
+ * layouts' constraints apply (WQ_EUNSUPPORTED); BF16 is rejected (WQ_EINVAL).
  */
-wq_status wq_dequantize(int fmt, const void* packed, const void* scales, const float* global_scale,
+wq_status wq_repack(int fmt, int64_t N, int64_t K, int32_t src_layout, const void* src_packed, const void* src_scales,
+                    int32_t dst_layout, void* dst_packed, void* dst_scales, void* stream);
+
+/*
+ * Dequantize packed weights (in `layout`) to bf16 W_out[N][K], row-major (the
+ * DQ of the two-kernel form, "TorchAO FP8 Weight-Only Quantization (Linear)",
+ * intro).  Each element is bf16(fp32 product) of the code's value and its
+ * scale(s), evaluated in the order code * block-scale * global-scale.
+ */
+wq_status wq_dequantize(int fmt, const void* packed, int32_t layout, const void* scales, const float* global_scale,
                         int64_t N, int64_t K, void* W_out, void* stream);
 
 /*
@@ -160,16 +197,25 @@ size_t wq_linear_workspace(int fmt, int64_t M, int64_t N, int64_t K);
  * in device memory and is dequantized in registers ahead of the bf16 matrix
  * cores (every weight-only page's intro: a DQ prologue into a high-precision
  * GEMM; activations stay bf16).
- *   packed       : packed codes as wq_pack writes them (BF16: the dense weight)
+ *   packed       : packed codes (BF16: the dense weight)
+ *   layout       : layout of `packed` and `scales` (WQ_LAYOUT_ROWS as wq_pack
+ *                  writes them, or WQ_LAYOUT_TILES after wq_repack)
  *   scales       : the format's scales (NULL for BF16)
  *   global_scale : NVFP4's device float, else NULL
  *   bias         : bf16 [N] or NULL
  * Kernel constraints: K % 32 == 0 for 4-bit formats, K % 16 for FP8, K % 8
  * for BF16 (WQ_EUNSUPPORTED otherwise).
+ * Numerics by M: up to 128 rows (the small-M kernels) INT4 groups are summed
+ * exactly as s * (sum_k x_k (code_k + 136) - 136 sum_k x_k) in fp32 (the
+ * INT4_ASYM bias is 128 + zero-point), i.e. the scale multiplies the group's
+ * fp32 partial sum; above that (the LDS-tiled kernels) each INT4 weight is
+ * first rounded to bf16(code * s) -- the wq_dequantize value -- and then
+ * multiplied.  The other formats' decoded weights are exact in bf16 at every
+ * M, so only the accumulation order differs.
  */
-wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* packed, const void* scales,
-                    const float* global_scale, const void* bias, int64_t N, void* Y, void* workspace,
-                    size_t workspace_bytes, void* stream);
+wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* packed, int32_t layout,
+                    const void* scales, const float* global_scale, const void* bias, int64_t N, void* Y,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Calibration observer ("TorchAO Static FP8 Quantization (Linear)", "Calibrate,
@@ -198,14 +244,16 @@ wq_status wq_fp8_quantize_act(const void* X, int64_t M, int64_t K, const float* 
  * in FP8): quantizes X with wq_fp8_quantize_act's rule, multiplies E4M3 x E4M3
  * on the FP8 matrix cores with fp32 accumulation, then
  * Y = bf16(acc * act_scale * w_scale[n] (+ bias[n])).
- * Wq: E4M3 codes [N][K] (wq_quantize(WQ_FP8) output), w_scale: float [N].
- * K % 16 == 0.  Workspace: wq_linear_workspace(WQ_FP8, M, N, K) plus M*K bytes
- * for the quantized activations -- query wq_fp8_static_workspace.
+ * Wq: E4M3 codes [N][K] (wq_quantize(WQ_FP8) output) in `layout`, w_scale:
+ * float [N].  K % 16 == 0.  Workspace: wq_linear_workspace(WQ_FP8, M, N, K)
+ * plus M*K bytes for the quantized activations -- query
+ * wq_fp8_static_workspace.  Every check of both launches runs before the
+ * first is enqueued.
  */
 size_t wq_fp8_static_workspace(int64_t M, int64_t N, int64_t K);
 wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float* act_scale, const void* Wq,
-                               const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
-                               size_t workspace_bytes, void* stream);
+                               int32_t layout, const float* w_scale, const void* bias, int64_t N, void* Y,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The FP8 x FP8 GEMM of the static path on activations that are already
@@ -218,7 +266,7 @@ wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float*
  * wq_fp8_linear_workspace bytes (0 for most shapes).
  */
 size_t wq_fp8_linear_workspace(int64_t M, int64_t N, int64_t K);
-wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_scale, const void* Wq,
+wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_scale, const void* Wq, int32_t layout,
                         const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
                         size_t workspace_bytes, void* stream);
 
@@ -231,7 +279,7 @@ wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_s
  *   Y = bf16(Q(H, act_scale2) . deq(W2q)^T * act_scale2 * w2_scale[n] (+ b2))
  * with the same per-step arithmetic as two wq_fp8_static_linear calls (results
  * differ only by fp32 accumulation order); H never leaves the chip.
- * W1q E4M3 [N1][K1], W2q E4M3 [N2][N1], scales float [N1] / [N2], biases bf16
+ * W1q E4M3 [N1][K1], W2q E4M3 [N2][N1] (WQ_LAYOUT_ROWS), scales float [N1] / [N2], biases bf16
  * or NULL.  K1 % 16 == 0, N1 % 16 == 0, M * K1 * 2 < 2^31, and 16 rows of the
  * input and hidden codes plus both layers' column scales and biases must fit
  * in the 160 KiB LDS of a CU (K1 + N1 up to about 9.5K; else WQ_EUNSUPPORTED --
@@ -255,17 +303,18 @@ wq_status wq_fp8_static_mlp2(const void* X, int64_t M, int64_t K1, const float* 
  *
  * wq_mx_linear: Y = bf16(sum_k deq(Xq)[m][k] deq(Wq)[n][k] (+ bias[n])) on the
  * E2M1 x E2M1 scaled matrix cores (fp32 accumulation).  Wq/Ws: the packed
- * weight and E8M0 scales of wq_quantize + wq_pack for WQ_MXFP4.  N % 32 == 0,
- * K % 32 == 0.  No workspace.
+ * weight and E8M0 scales of wq_quantize + wq_pack for WQ_MXFP4, in `layout`
+ * (the activations Xq/Xs are always row-major).  N % 32 == 0, K % 32 == 0.
+ * No workspace.
  *
  * wq_mxfp4_dynamic_linear: wq_mx_quantize_act into the workspace, then
  * wq_mx_linear.  Workspace: wq_mxfp4_dynamic_workspace(M, K) bytes.
  */
 wq_status wq_mx_quantize_act(const void* X, int64_t M, int64_t K, void* Xq, void* Xs, void* stream);
-wq_status wq_mx_linear(const void* Xq, const void* Xs, int64_t M, int64_t K, const void* Wq, const void* Ws,
-                       const void* bias, int64_t N, void* Y, void* stream);
+wq_status wq_mx_linear(const void* Xq, const void* Xs, int64_t M, int64_t K, const void* Wq, int32_t layout,
+                       const void* Ws, const void* bias, int64_t N, void* Y, void* stream);
 size_t wq_mxfp4_dynamic_workspace(int64_t M, int64_t K);
-wq_status wq_mxfp4_dynamic_linear(const void* X, int64_t M, int64_t K, const void* Wq, const void* Ws,
+wq_status wq_mxfp4_dynamic_linear(const void* X, int64_t M, int64_t K, const void* Wq, int32_t layout, const void* Ws,
                                   const void* bias, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
                                   void* stream);
 

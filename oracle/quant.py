@@ -347,6 +347,52 @@ def dequant(fmt, codes, scales, g=None):
     raise ValueError(fmt)
 
 
+# ------------------------------------------------------------------ kernel tile order
+
+
+TILE_ROWS, TILE_BYTES, TILE_K = 16, 64, 128
+SCALE_TILE_BYTES = {"int4": 2, "int4_asym": 4, "nvfp4": 8, "mxfp4": 4}
+
+
+def tile_order(fmt, packed, scales):
+    """The kernel tile order of a packed weight and its block scales (the
+    one-time re-layout of the packed constant, "TorchAO INT4 Weight-Only
+    Quantization (Linear)", "Export and compile").  Layout definition: the
+    packed rows are cut into tiles of 16 rows x 64 bytes; tiles are taken
+    row group by row group, and within a row group column block by column
+    block; a tile stores its 16 rows' 64 bytes one after the other.  The block
+    scales of 128 K per row (2, 4, 8 or 4 bytes for INT4, INT4_ASYM, NVFP4,
+    MXFP4) follow the same tiles.  FP8 row scales are returned unchanged.
+
+    packed: uint8 [N, row_bytes]; scales: the format's scale array (row-major,
+    any dtype).  Returns (packed_t uint8 [N * row_bytes], scales_t uint8 bytes
+    or the FP8 float array)."""
+    p = np.asarray(packed, np.uint8)
+    N, rb = p.shape
+    if N % TILE_ROWS or rb % TILE_BYTES:
+        raise ValueError("tile order needs N % 16 == 0 and row bytes % 64 == 0")
+    out = np.empty(N * rb, np.uint8)
+    pos = 0
+    for g in range(N // TILE_ROWS):
+        for j in range(rb // TILE_BYTES):
+            for r in range(TILE_ROWS):
+                out[pos:pos + TILE_BYTES] = p[g * TILE_ROWS + r, j * TILE_BYTES:(j + 1) * TILE_BYTES]
+                pos += TILE_BYTES
+    if fmt == "fp8":
+        return out, np.asarray(scales, np.float32)
+    sb = SCALE_TILE_BYTES[fmt]
+    sbytes = np.ascontiguousarray(scales).view(np.uint8).reshape(N, -1)
+    tiles = sbytes.shape[1] // sb
+    st = np.empty(sbytes.size, np.uint8)
+    pos = 0
+    for g in range(N // TILE_ROWS):
+        for j in range(tiles):
+            for r in range(TILE_ROWS):
+                st[pos:pos + sb] = sbytes[g * TILE_ROWS + r, j * sb:(j + 1) * sb]
+                pos += sb
+    return out, st
+
+
 def packed_weight(fmt, codes):
     """The byte stream the GEMM reads: nibble-packed for the 4-bit formats,
     the E4M3 code bytes themselves for FP8."""

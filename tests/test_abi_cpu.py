@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     L = wq.lib()
-    assert L.wq_abi_version() == 1
+    assert L.wq_abi_version() == 2
     assert L.wq_status_str(0) == b"WQ_OK"
     assert L.wq_status_str(2) == b"WQ_ESHAPE"
     assert L.wq_status_str(99) == b"WQ_UNKNOWN"
@@ -55,10 +55,10 @@ def test_shape_rules(fmt, N, K):
     assert e.value.status == wq.ESHAPE
 
 
-def _call_linear(fmt=1, X=16, M=32, K=256, W=32, S=48, G=None, B=None, N=64, Y=64, ws=None, wsb=0):
+def _call_linear(fmt=1, X=16, M=32, K=256, W=32, S=48, G=None, B=None, N=64, Y=64, ws=None, wsb=0, layout=0):
     L = wq.lib()
     v = ctypes.c_void_p
-    return L.wq_linear(fmt, v(X), M, K, v(W), v(S), v(G), v(B), N, v(Y), v(ws), wsb, None)
+    return L.wq_linear(fmt, v(X), M, K, v(W), layout, v(S), v(G), v(B), N, v(Y), v(ws), wsb, None)
 
 
 def test_linear_host_validation():
@@ -98,37 +98,40 @@ def test_quantize_pack_dequant_validation():
     assert L.wq_quantize(2, None, 0, 64, None, None, None, None) == wq.OK
     assert L.wq_pack(0, v(16), 64, 64, v(16), None) == wq.EINVAL
     assert L.wq_pack(4, v(16), 64, 40, v(16), None) == wq.ESHAPE
-    assert L.wq_dequantize(3, v(16), v(16), None, 64, 64, v(16), None) == wq.EINVAL
-    assert L.wq_dequantize(2, v(16), v(16), None, 64, 12, v(16), None) == wq.EUNSUPPORTED
+    assert L.wq_dequantize(3, v(16), 0, v(16), None, 64, 64, v(16), None) == wq.EINVAL
+    assert L.wq_dequantize(2, v(16), 0, v(16), None, 64, 12, v(16), None) == wq.EUNSUPPORTED
+    assert L.wq_dequantize(4, v(16), 1, v(16), None, 64, 96, v(16), None) == wq.EUNSUPPORTED  # tiles: K % 128
     assert L.wq_fp8_quantize_act(v(16), 4, 16, None, v(16), None) == wq.EINVAL
     assert L.wq_fp8_quantize_act(v(16), 1 << 22, 1 << 21, v(16), v(16), None) == wq.EUNSUPPORTED  # 2^43 elements
-    assert L.wq_fp8_static_linear(v(16), 4, 24, v(16), v(16), v(16), None, 16, v(16), v(16), 1 << 20,
+    assert L.wq_fp8_static_linear(v(16), 4, 24, v(16), v(16), 0, v(16), None, 16, v(16), v(16), 1 << 20,
                                   None) == wq.EUNSUPPORTED
-    assert L.wq_fp8_static_linear(v(16), 4, 32, v(16), v(16), v(16), None, 16, v(16), None, 0,
+    assert L.wq_fp8_static_linear(v(16), 4, 32, v(16), v(16), 0, v(16), None, 16, v(16), None, 0,
                                   None) == wq.EWORKSPACE
     assert L.wq_absmax(None, 10, v(16), None) == wq.EINVAL
     assert L.wq_absmax(None, 0, None, None) == wq.OK
     # FP8 GEMM on pre-quantized activations
-    assert L.wq_fp8_linear(v(16), 4, 24, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.EUNSUPPORTED
-    assert L.wq_fp8_linear(v(16), 4, 32, None, v(16), v(16), None, 16, v(16), None, 0, None) == wq.EINVAL
-    assert L.wq_fp8_linear(v(8), 4, 32, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.EALIGN
-    assert L.wq_fp8_linear(v(16), 0, 32, v(16), v(16), v(16), None, 16, v(16), None, 0, None) == wq.OK
-    assert L.wq_fp8_linear(v(16), 32, 4096, v(16), v(16), v(16), None, 256, v(16), None, 0,
+    assert L.wq_fp8_linear(v(16), 4, 24, v(16), v(16), 0, v(16), None, 16, v(16), None, 0, None) == wq.EUNSUPPORTED
+    assert L.wq_fp8_linear(v(16), 4, 32, None, v(16), 0, v(16), None, 16, v(16), None, 0, None) == wq.EINVAL
+    assert L.wq_fp8_linear(v(8), 4, 32, v(16), v(16), 0, v(16), None, 16, v(16), None, 0, None) == wq.EALIGN
+    assert L.wq_fp8_linear(v(16), 0, 32, v(16), v(16), 0, v(16), None, 16, v(16), None, 0, None) == wq.OK
+    assert L.wq_fp8_linear(v(16), 32, 4096, v(16), v(16), 0, v(16), None, 256, v(16), None, 0,
                            None) == wq.EWORKSPACE  # narrow layer: split K
     # MXFP4 dynamic-activation path
     assert L.wq_mx_quantize_act(v(16), 4, 48, v(16), v(16), None) == wq.ESHAPE
     assert L.wq_mx_quantize_act(v(16), 4, 64, None, v(16), None) == wq.EINVAL
     assert L.wq_mx_quantize_act(v(8), 4, 64, v(16), v(16), None) == wq.EALIGN
     assert L.wq_mx_quantize_act(None, 0, 64, None, None, None) == wq.OK
-    assert L.wq_mx_linear(v(16), v(16), 4, 64, v(16), v(16), None, 48, v(16), None) == wq.ESHAPE  # N % 32
-    assert L.wq_mx_linear(v(16), v(16), 4, 48, v(16), v(16), None, 64, v(16), None) == wq.ESHAPE  # K % 32
-    assert L.wq_mx_linear(v(16), None, 4, 64, v(16), v(16), None, 64, v(16), None) == wq.EINVAL
-    assert L.wq_mx_linear(v(16), v(16), 4, 64, v(16), v(16), None, 64, v(24), None) == wq.EALIGN
+    assert L.wq_mx_linear(v(16), v(16), 4, 64, v(16), 0, v(16), None, 48, v(16), None) == wq.ESHAPE  # N % 32
+    assert L.wq_mx_linear(v(16), v(16), 4, 48, v(16), 0, v(16), None, 64, v(16), None) == wq.ESHAPE  # K % 32
+    assert L.wq_mx_linear(v(16), None, 4, 64, v(16), 0, v(16), None, 64, v(16), None) == wq.EINVAL
+    assert L.wq_mx_linear(v(16), v(16), 4, 64, v(16), 0, v(16), None, 64, v(24), None) == wq.EALIGN
     need = wq.wq_mxfp4_dynamic_workspace(32, 3072)
     assert need >= 32 * 1536 + 32 * 96
-    assert L.wq_mxfp4_dynamic_linear(v(16), 32, 3072, v(16), v(16), None, 4096, v(16), v(16), need - 1,
+    assert L.wq_mxfp4_dynamic_linear(v(16), 32, 3072, v(16), 0, v(16), None, 4096, v(16), v(16), need - 1,
                                      None) == wq.EWORKSPACE
-    assert L.wq_mxfp4_dynamic_linear(v(16), 0, 3072, v(16), v(16), None, 4096, v(16), None, 0, None) == wq.OK
+    assert L.wq_mxfp4_dynamic_linear(v(16), 0, 3072, v(16), 0, v(16), None, 4096, v(16), None, 0, None) == wq.OK
+    assert L.wq_mxfp4_dynamic_linear(v(16), 4, 96, v(16), 1, v(16), None, 64, v(16), v(16), 1 << 20,
+                                     None) == wq.EUNSUPPORTED  # tiles need K % 128
     # fused static MLP
     mlp = lambda M=32, K1=256, N1=512, N2=128, X=16: L.wq_fp8_static_mlp2(
         v(X), M, K1, v(16), v(16), v(16), None, N1, v(16), v(16), v(16), None, N2, v(16), None)
@@ -159,3 +162,52 @@ def test_workspace_plans_are_consistent():
     # wide layers have enough workgroups without K splits
     assert wq.wq_linear_workspace("mxfp4", 4096, 4096, 3072) == 0
     assert wq.wq_linear_workspace("int4", 32, 4096, 3072) == 0
+
+
+def _launch_attempts():
+    """Launch attempts so far in the sanitizer host-check build (None in the
+    real library, where a launch without a GPU fails with WQ_EHIP instead)."""
+    f = getattr(wq.lib(), "wq_hostcheck_launches", None)
+    if f is None:
+        return None
+    f.restype = ctypes.c_long
+    return f()
+
+
+def test_static_linear_validates_both_launches_first():
+    """The static-FP8 Linear runs two kernels (activation Q, then the FP8
+    GEMM); a GEMM-only limit (K of 2^22 or more) must be rejected before the
+    first one is enqueued: the status is WQ_EUNSUPPORTED, not the WQ_EHIP a
+    launch attempt gives without a GPU, and no launch was attempted."""
+    L = wq.lib()
+    v = ctypes.c_void_p
+    K = 1 << 22
+    need = wq.wq_fp8_static_workspace(1, 16, K)
+    before = _launch_attempts()
+    assert L.wq_fp8_static_linear(v(16), 1, K, v(16), v(16), 0, v(16), None, 16, v(16), v(256), need, None) == \
+        wq.EUNSUPPORTED
+    assert b"2^22" in L.wq_last_error()
+    assert _launch_attempts() == before
+
+
+def test_layout_validation():
+    """Tile order (layout 1) needs whole 16-row x 64-byte tiles; BF16 has only
+    the rows layout; unknown layouts are rejected -- all before any launch."""
+    assert _call_linear(layout=2) == wq.EINVAL
+    assert _call_linear(fmt=0, K=256, S=None, layout=1) == wq.EUNSUPPORTED  # BF16
+    assert _call_linear(fmt=1, N=40, layout=1) == wq.EUNSUPPORTED  # N % 16
+    assert _call_linear(fmt=4, K=96, layout=1) == wq.EUNSUPPORTED  # 4-bit: K % 128
+    assert _call_linear(fmt=2, K=96, layout=1) == wq.EUNSUPPORTED  # FP8: K % 64
+    assert _call_linear(fmt=2, M=0, K=128, layout=1) == wq.OK  # empty call
+    L = wq.lib()
+    v = ctypes.c_void_p
+    assert L.wq_repack(0, 64, 256, 0, v(16), v(16), 1, v(32), v(32), None) == wq.EINVAL  # BF16
+    assert L.wq_repack(4, 64, 256, 0, v(16), v(16), 3, v(32), v(32), None) == wq.EINVAL  # layout 3
+    assert L.wq_repack(4, 48, 256, 0, v(16), v(16), 1, v(32), v(32), None) == wq.ESHAPE  # MXFP4 N % 32
+    assert L.wq_repack(1, 40, 256, 0, v(16), v(16), 1, v(32), v(32), None) == wq.EUNSUPPORTED  # tiles: N % 16
+    assert L.wq_repack(1, 64, 256, 0, v(16), v(16), 1, v(16), v(32), None) == wq.EINVAL  # in place
+    assert L.wq_repack(1, 64, 256, 0, None, v(16), 1, v(32), v(32), None) == wq.EINVAL
+    assert L.wq_repack(1, 64, 256, 0, v(16), v(8), 1, v(32), v(48), None) == wq.EALIGN
+    assert L.wq_repack(1, 0, 256, 0, None, None, 1, None, None, None) == wq.OK
+    assert L.wq_fp8_linear(v(16), 4, 96, v(16), v(16), 1, v(16), None, 16, v(16), None, 0, None) == wq.EUNSUPPORTED
+    assert L.wq_mx_linear(v(16), v(16), 4, 96, v(16), 1, v(16), None, 64, v(16), None) == wq.EUNSUPPORTED

@@ -302,3 +302,48 @@ def test_dequant_fp8_row_reconstruction_bound():
     assert bound_ok(Q.dequant_fp8_row(codes, s))
     assert not bound_ok(Q.dequant_fp8_row(codes, np.roll(s, 1)))
     assert not bound_ok(C.e4m3_decode(codes) / sd)
+
+
+# ------------------------------------------------------------------ kernel tile order
+
+
+def test_tile_order_hand_example():
+    """32 rows x 128 bytes (two row groups, two column blocks): byte b of row n
+    lands at ((n // 16) * 2 + b // 64) * 1024 + 64 * (n % 16) + b % 64."""
+    N, rb = 32, 128
+    packed = np.arange(N * rb, dtype=np.int64).reshape(N, rb)
+    tag = (packed % 251).astype(np.uint8)  # distinct enough to catch a swapped index
+    got, _ = Q.tile_order("mxfp4", tag, np.zeros((N, 8), np.uint8))
+    for n, b in [(0, 0), (0, 63), (0, 64), (1, 0), (15, 127), (16, 0), (17, 65), (31, 127)]:
+        at = ((n // 16) * 2 + b // 64) * 1024 + 64 * (n % 16) + b % 64
+        assert got[at] == tag[n, b], (n, b)
+    # a single tile (16 rows x 64 bytes) is its own row-major order
+    one = np.arange(16 * 64, dtype=np.int64).astype(np.uint8).reshape(16, 64)
+    assert np.array_equal(Q.tile_order("int4", one, np.zeros((16, 1), np.uint16))[0], one.ravel())
+
+
+@pytest.mark.parametrize("fmt,sb", [("int4", 2), ("nvfp4", 8), ("mxfp4", 4)])
+def test_tile_order_scales_follow_the_tiles(fmt, sb):
+    """The scale bytes of row n for K range [128 j, 128 j + 128) sit at
+    ((n // 16) * (K // 128) + j) * 16 * sb + sb * (n % 16)."""
+    N, K = 32, 384
+    W = synth.linear_weight(N, K, 41)
+    codes, scales, _ = Q.quantize(fmt, W)
+    packed = Q.packed_weight(fmt, codes)
+    pt, st = Q.tile_order(fmt, packed, scales)
+    sbytes = np.ascontiguousarray(scales).view(np.uint8).reshape(N, -1)
+    T = K // 128
+    for n in (0, 5, 16, 31):
+        for j in range(T):
+            at = ((n // 16) * T + j) * 16 * sb + sb * (n % 16)
+            assert st[at:at + sb].tolist() == sbytes[n, j * sb:(j + 1) * sb].tolist()
+    # both orders hold the same bytes
+    assert sorted(pt.tolist()) == sorted(packed.ravel().tolist())
+    assert sorted(st.tolist()) == sorted(sbytes.ravel().tolist())
+
+
+def test_tile_order_rejects_partial_tiles():
+    with pytest.raises(ValueError):
+        Q.tile_order("int4", np.zeros((24, 64), np.uint8), np.zeros((24, 1), np.uint16))
+    with pytest.raises(ValueError):
+        Q.tile_order("fp8", np.zeros((16, 96), np.uint8), np.zeros(16, np.float32))

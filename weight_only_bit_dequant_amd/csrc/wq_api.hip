@@ -1,7 +1,7 @@
 // C ABI (include/wq.h): argument validation, layout queries and dispatch to
 // the kernel launchers.  Host-side checks run before any HIP call, so every
 // error path is reachable without a GPU.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
 #include <cstdio>
@@ -62,6 +62,20 @@ wq_status check_shape_rule(int f, int64_t N, int64_t K) {
     return fail(WQ_ESHAPE, "NVFP4 needs N %% 16 == 0 and K %% 16 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
   if (f == WQ_MXFP4 && (N % 32 || K % 32))
     return fail(WQ_ESHAPE, "MXFP4 needs N %% 32 == 0 and K %% 32 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
+  return WQ_OK;
+}
+
+// Weight layouts: rows (0) for every format; tile order (1) for the quantized
+// formats when whole 16-row x 64-byte tiles cover the weight.
+wq_status check_layout(int f, int32_t layout, int64_t N, int64_t K) {
+  if (layout != WQ_LAYOUT_ROWS && layout != WQ_LAYOUT_TILES) return fail(WQ_EINVAL, "unknown layout %d", (int)layout);
+  if (layout == WQ_LAYOUT_TILES) {
+    if (f == WQ_BF16) return fail(WQ_EUNSUPPORTED, "BF16 weights have only the rows layout");
+    const int64_t kmul = f == WQ_FP8 ? 64 : 128;
+    if (N % 16 || K % kmul)
+      return fail(WQ_EUNSUPPORTED, "tile order needs N %% 16 == 0 and K %% %lld == 0 (N=%lld K=%lld)", (long long)kmul,
+                  (long long)N, (long long)K);
+  }
   return WQ_OK;
 }
 
@@ -152,10 +166,12 @@ wq_status wq_pack(int fmt, const void* codes, int64_t N, int64_t K, void* packed
                     "wq_pack launch");
 }
 
-wq_status wq_dequantize(int fmt, const void* packed, const void* scales, const float* global_scale,
+wq_status wq_dequantize(int fmt, const void* packed, int32_t layout, const void* scales, const float* global_scale,
                         int64_t N, int64_t K, void* W_out, void* stream) {
   if (!valid_fmt(fmt)) return fail(WQ_EINVAL, "wq_dequantize: unknown format %d", fmt);
   wq_status st = check_shape_rule(fmt, N, K);
+  if (st != WQ_OK) return st;
+  st = check_layout(fmt, layout, N, K);
   if (st != WQ_OK) return st;
   if (N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
   if (N == 0 || K == 0) return ok();
@@ -163,9 +179,35 @@ wq_status wq_dequantize(int fmt, const void* packed, const void* scales, const f
   if (fmt == WQ_NVFP4 && !global_scale) return fail(WQ_EINVAL, "wq_dequantize: NVFP4 needs global_scale");
   if (K % 8) return fail(WQ_EUNSUPPORTED, "wq_dequantize: K %% 8 != 0");
   if (!aligned16(packed) || !aligned16(W_out)) return fail(WQ_EALIGN, "wq_dequantize: buffers must be 16-byte aligned");
-  return hip_status(wq::launch_dequantize(kfmt_of(fmt), packed, scales, global_scale, N, K, (uint16_t*)W_out,
+  return hip_status(wq::launch_dequantize(kfmt_of(fmt), layout, packed, scales, global_scale, N, K, (uint16_t*)W_out,
                                           (hipStream_t)stream),
                     "wq_dequantize launch");
+}
+
+wq_status wq_repack(int fmt, int64_t N, int64_t K, int32_t src_layout, const void* src_packed, const void* src_scales,
+                    int32_t dst_layout, void* dst_packed, void* dst_scales, void* stream) {
+  if (!valid_fmt(fmt) || fmt == WQ_BF16) return fail(WQ_EINVAL, "wq_repack: unsupported format %d", fmt);
+  wq_status st = check_shape_rule(fmt, N, K);
+  if (st != WQ_OK) return st;
+  st = check_layout(fmt, src_layout, N, K);
+  if (st != WQ_OK) return st;
+  st = check_layout(fmt, dst_layout, N, K);
+  if (st != WQ_OK) return st;
+  if (N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  if (N == 0 || K == 0) return ok();
+  if (!src_packed || !src_scales || !dst_packed || !dst_scales) return fail(WQ_EINVAL, "wq_repack: null pointer");
+  if (src_packed == dst_packed || src_scales == dst_scales)
+    return fail(WQ_EINVAL, "wq_repack: source and destination must be distinct buffers");
+  if (!aligned16(src_packed) || !aligned16(dst_packed) || !aligned16(src_scales) || !aligned16(dst_scales))
+    return fail(WQ_EALIGN, "wq_repack: buffers must be 16-byte aligned");
+  // rows layout with row bytes not a multiple of 16 is copied in 16-byte chunks: keep whole chunks per row
+  if ((fmt == WQ_FP8 ? K : K / 2) % 16)
+    return fail(WQ_EUNSUPPORTED, "wq_repack: rows of a multiple of 16 bytes needed (K=%lld)", (long long)K);
+  if (fmt != WQ_FP8 && K % 128)
+    return fail(WQ_EUNSUPPORTED, "wq_repack: block scales are moved per 128-K tile (K=%lld)", (long long)K);
+  return hip_status(wq::launch_repack(kfmt_of(fmt), N, K, src_layout, src_packed, src_scales, dst_layout, dst_packed,
+                                      dst_scales, (hipStream_t)stream),
+                    "wq_repack launch");
 }
 
 size_t wq_linear_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
@@ -173,15 +215,25 @@ size_t wq_linear_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
   return wq::plan_linear(kfmt_of(fmt), M, N, K).ws_bytes;
 }
 
-static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int64_t K, const void* W,
-                               const void* scales, const float* gscale, const float* act_scale, const void* bias,
-                               int64_t N, void* Y, void* ws, size_t ws_bytes, void* stream) {
+// Host-side checks of a dequant-GEMM call; on success fills the launch
+// arguments and the plan.  Nothing is enqueued here, so callers that launch
+// more than one kernel validate every launch before the first one.
+static wq_status linear_check(int kfmt, int fmt, const void* X, int64_t M, int64_t K, const void* W, int32_t layout,
+                              const void* scales, const float* gscale, const float* act_scale, const void* bias,
+                              int64_t N, void* Y, void* ws, size_t ws_bytes, wq::LinearArgs* a, wq::LinearPlan* p,
+                              bool* empty) {
+  *empty = false;
   if (!valid_fmt(fmt)) return fail(WQ_EINVAL, "unknown format %d", fmt);
   if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
   wq_status st = check_shape_rule(fmt, N, K);
   if (st != WQ_OK) return st;
+  st = check_layout(fmt, layout, N, K);
+  if (st != WQ_OK) return st;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
-  if (M == 0 || N == 0) return ok();
+  if (M == 0 || N == 0) {
+    *empty = true;
+    return ok();
+  }
   if (K == 0) return fail(WQ_EUNSUPPORTED, "K == 0");
   if (K % kernel_k_multiple(fmt))
     return fail(WQ_EUNSUPPORTED, "%s linear kernels need K %% %d == 0 (K=%lld)", fmt_name(fmt),
@@ -201,32 +253,45 @@ static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int6
   if (kfmt != wq::KF_NVFP4 && gscale) return fail(WQ_EINVAL, "global_scale must be NULL for %s", fmt_name(fmt));
   if (kfmt == wq::KF_FP8S && !act_scale) return fail(WQ_EINVAL, "null act_scale");
   if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return fail(WQ_EALIGN, "X, weight and Y must be 16-byte aligned");
-  const wq::LinearPlan p = wq::plan_linear(kfmt, M, N, K);
-  if (p.ws_bytes > 0) {
-    if (!ws || ws_bytes < p.ws_bytes)
-      return fail(WQ_EWORKSPACE, "workspace of %zu bytes required (got %zu)", p.ws_bytes, ws ? ws_bytes : (size_t)0);
+  *p = wq::plan_linear(kfmt, M, N, K);
+  if (p->ws_bytes > 0) {
+    if (!ws || ws_bytes < p->ws_bytes)
+      return fail(WQ_EWORKSPACE, "workspace of %zu bytes required (got %zu)", p->ws_bytes, ws ? ws_bytes : (size_t)0);
     if (!aligned16(ws)) return fail(WQ_EALIGN, "workspace must be 16-byte aligned");
   }
-  wq::LinearArgs a{};
-  a.X = X;
-  a.W = W;
-  a.scales = scales;
-  a.gscale = gscale;
-  a.act_scale = act_scale;
-  a.bias = (const uint16_t*)bias;
-  a.Y = (uint16_t*)Y;
-  a.part = p.ws_bytes ? (float*)ws : nullptr;
-  a.M = (int)M;
-  a.N = (int)N;
-  a.K = (int)K;
+  *a = wq::LinearArgs{};
+  a->X = X;
+  a->W = W;
+  a->scales = scales;
+  a->gscale = gscale;
+  a->act_scale = act_scale;
+  a->bias = (const uint16_t*)bias;
+  a->Y = (uint16_t*)Y;
+  a->part = p->ws_bytes ? (float*)ws : nullptr;
+  a->M = (int)M;
+  a->N = (int)N;
+  a->K = (int)K;
+  a->wl = layout;
+  return WQ_OK;
+}
+
+static wq_status linear_common(int kfmt, int fmt, const void* X, int64_t M, int64_t K, const void* W,
+                               int32_t layout, const void* scales, const float* gscale, const float* act_scale,
+                               const void* bias, int64_t N, void* Y, void* ws, size_t ws_bytes, void* stream) {
+  wq::LinearArgs a;
+  wq::LinearPlan p;
+  bool empty;
+  wq_status st = linear_check(kfmt, fmt, X, M, K, W, layout, scales, gscale, act_scale, bias, N, Y, ws, ws_bytes, &a,
+                              &p, &empty);
+  if (st != WQ_OK || empty) return st;
   return hip_status(wq::launch_linear(kfmt, a, p, (hipStream_t)stream), "wq_linear launch");
 }
 
-wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* packed, const void* scales,
-                    const float* global_scale, const void* bias, int64_t N, void* Y, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  return linear_common(kfmt_of(fmt), fmt, X, M, K, packed, scales, global_scale, nullptr, bias, N, Y, workspace,
-                       workspace_bytes, stream);
+wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* packed, int32_t layout,
+                    const void* scales, const float* global_scale, const void* bias, int64_t N, void* Y,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_common(kfmt_of(fmt), fmt, X, M, K, packed, layout, scales, global_scale, nullptr, bias, N, Y,
+                       workspace, workspace_bytes, stream);
 }
 
 wq_status wq_absmax(const void* X, int64_t numel, float* amax, void* stream) {
@@ -267,8 +332,8 @@ size_t wq_fp8_static_workspace(int64_t M, int64_t N, int64_t K) {
 }
 
 wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float* act_scale, const void* Wq,
-                               const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               int32_t layout, const float* w_scale, const void* bias, int64_t N, void* Y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
   if (M == 0 || N == 0) return ok();
   if (K > 0 && K % 16) return fail(WQ_EUNSUPPORTED, "static FP8 linear needs K %% 16 == 0 (K=%lld)", (long long)K);
@@ -281,11 +346,19 @@ wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float*
   if (!X || !act_scale || !Wq || !w_scale || !Y) return fail(WQ_EINVAL, "wq_fp8_static_linear: null pointer");
   if (!aligned16(X) || !aligned16(Wq) || !aligned16(Y))
     return fail(WQ_EALIGN, "X, Wq and Y must be 16-byte aligned");
+  if (M * K >= ((int64_t)1 << 43)) return fail(WQ_EUNSUPPORTED, "wq_fp8_static_linear: 2^43 activations or more");
+  // both launches are validated before the first is enqueued
   void* xq = (char*)workspace + static_xq_offset(M, N, K);
-  wq_status st = wq_fp8_quantize_act(X, M, K, act_scale, xq, stream);
+  wq::LinearArgs a;
+  wq::LinearPlan p;
+  bool empty;
+  wq_status st = linear_check(wq::KF_FP8S, WQ_FP8, xq, M, K, Wq, layout, w_scale, nullptr, act_scale, bias, N, Y,
+                              workspace, workspace_bytes, &a, &p, &empty);
   if (st != WQ_OK) return st;
-  return linear_common(wq::KF_FP8S, WQ_FP8, xq, M, K, Wq, w_scale, nullptr, act_scale, bias, N, Y, workspace,
-                       workspace_bytes, stream);
+  st = hip_status(wq::launch_quantize_act((const uint16_t*)X, M * K, act_scale, (uint8_t*)xq, (hipStream_t)stream),
+                  "wq_fp8_quantize_act launch");
+  if (st != WQ_OK) return st;
+  return hip_status(wq::launch_linear(wq::KF_FP8S, a, p, (hipStream_t)stream), "wq_linear launch");
 }
 
 size_t wq_fp8_linear_workspace(int64_t M, int64_t N, int64_t K) {
@@ -293,14 +366,14 @@ size_t wq_fp8_linear_workspace(int64_t M, int64_t N, int64_t K) {
   return wq::plan_linear(wq::KF_FP8S, M, N, K).ws_bytes;
 }
 
-wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_scale, const void* Wq,
+wq_status wq_fp8_linear(const void* Xq, int64_t M, int64_t K, const float* act_scale, const void* Wq, int32_t layout,
                         const float* w_scale, const void* bias, int64_t N, void* Y, void* workspace,
                         size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
   if (M == 0 || N == 0) return ok();
   if (K > 0 && K % 16) return fail(WQ_EUNSUPPORTED, "FP8 linear needs K %% 16 == 0 (K=%lld)", (long long)K);
   if (!Xq || !act_scale || !Wq || !w_scale || !Y) return fail(WQ_EINVAL, "wq_fp8_linear: null pointer");
-  return linear_common(wq::KF_FP8S, WQ_FP8, Xq, M, K, Wq, w_scale, nullptr, act_scale, bias, N, Y, workspace,
+  return linear_common(wq::KF_FP8S, WQ_FP8, Xq, M, K, Wq, layout, w_scale, nullptr, act_scale, bias, N, Y, workspace,
                        workspace_bytes, stream);
 }
 
@@ -317,10 +390,12 @@ wq_status wq_mx_quantize_act(const void* X, int64_t M, int64_t K, void* Xq, void
                     "wq_mx_quantize_act launch");
 }
 
-wq_status wq_mx_linear(const void* Xq, const void* Xs, int64_t M, int64_t K, const void* Wq, const void* Ws,
-                       const void* bias, int64_t N, void* Y, void* stream) {
+wq_status wq_mx_linear(const void* Xq, const void* Xs, int64_t M, int64_t K, const void* Wq, int32_t layout,
+                       const void* Ws, const void* bias, int64_t N, void* Y, void* stream) {
   if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
   wq_status st = check_shape_rule(WQ_MXFP4, N, K);
+  if (st != WQ_OK) return st;
+  st = check_layout(WQ_MXFP4, layout, N, K);
   if (st != WQ_OK) return st;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
   if (M == 0 || N == 0) return ok();
@@ -340,6 +415,7 @@ wq_status wq_mx_linear(const void* Xq, const void* Xs, int64_t M, int64_t K, con
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
+  a.wl = layout;
   return hip_status(wq::launch_mx_linear(a, (hipStream_t)stream), "wq_mx_linear launch");
 }
 
@@ -348,11 +424,13 @@ size_t wq_mxfp4_dynamic_workspace(int64_t M, int64_t K) {
   return align256((size_t)M * (size_t)K / 2) + align256((size_t)M * (size_t)(K / 32));
 }
 
-wq_status wq_mxfp4_dynamic_linear(const void* X, int64_t M, int64_t K, const void* Wq, const void* Ws,
+wq_status wq_mxfp4_dynamic_linear(const void* X, int64_t M, int64_t K, const void* Wq, int32_t layout, const void* Ws,
                                   const void* bias, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
   wq_status st = check_shape_rule(WQ_MXFP4, N, K);
+  if (st != WQ_OK) return st;
+  st = check_layout(WQ_MXFP4, layout, N, K);
   if (st != WQ_OK) return st;
   if (M == 0 || N == 0) return ok();
   const size_t need = wq_mxfp4_dynamic_workspace(M, K);
@@ -370,7 +448,7 @@ wq_status wq_mxfp4_dynamic_linear(const void* X, int64_t M, int64_t K, const voi
     return fail(WQ_EUNSUPPORTED, "buffer of 2^31 bytes or more, or K of 2^22 or more");
   st = wq_mx_quantize_act(X, M, K, xq, xs, stream);
   if (st != WQ_OK) return st;
-  return wq_mx_linear(xq, xs, M, K, Wq, Ws, bias, N, Y, stream);
+  return wq_mx_linear(xq, xs, M, K, Wq, layout, Ws, bias, N, Y, stream);
 }
 
 wq_status wq_fp8_static_mlp2(const void* X, int64_t M, int64_t K1, const float* act_scale1, const void* W1q,

@@ -112,7 +112,7 @@ constexpr int decoded_bytes() {
 
 // WGN: waves along N in a 2 x WGN wave grid (GT = 128 * WGN threads per K
 // group); each wave owns a (BM/2) x (BN/WGN) block of the tile.
-template <int F, int BM, int BN, int STG, int KS, int WGN>
+template <int F, int BM, int BN, int STG, int KS, int WGN, int WL>
 __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
   using TF = TileFmt<F>;
   constexpr int GT = 128 * WGN;                // threads per K group
@@ -192,11 +192,10 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
       const int k0 = kbeg + kt * kBK + part * kpc;
       const bool ok = k0 < kend;
       const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : ((F == KF_FP8) ? (uint32_t)k0 : (uint32_t)k0 / 2u);
-      wb[q] = bload128(Wr, off_if(ok, n * wrow + byte0));
-      if constexpr (F == KF_INT4) sb[q] = bload16(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u));
-      else if constexpr (F == KF_INT4A) sb[q] = bload32(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 4u));
-      else if constexpr (F == KF_NVFP4) sb[q] = bload16(Sr, off_if(ok, n * (uint32_t)(K / 16) + (uint32_t)(k0 / 16)));
-      else if constexpr (F == KF_MXFP4) sb[q] = bload8(Sr, off_if(ok, n * (uint32_t)(K / 32) + (uint32_t)(k0 / 32)));
+      wb[q] = bload128(Wr, off_if(ok, w_off<WL>(n, byte0, wrow)));
+      if constexpr (F == KF_INT4 || F == KF_NVFP4) sb[q] = bload16(Sr, off_if(ok, s_off<F, WL>(n, (uint32_t)k0, (uint32_t)K)));
+      else if constexpr (F == KF_INT4A) sb[q] = bload32(Sr, off_if(ok, s_off<F, WL>(n, (uint32_t)k0, (uint32_t)K)));
+      else if constexpr (F == KF_MXFP4) sb[q] = bload8(Sr, off_if(ok, s_off<F, WL>(n, (uint32_t)k0, (uint32_t)K)));
       else sb[q] = 0u;
     }
   };
@@ -367,7 +366,7 @@ __global__ __launch_bounds__(128 * WGN * KS) void k_gemm_tiled(LinearArgs a) {
 // the other LDS stage at the end of step k.  Two LDS stages of 64 KiB, one
 // barrier per step: after it a wave issues the next step's activation loads
 // and the weight loads two steps ahead, runs its MFMAs, then decodes.
-template <int F, int NW>
+template <int F, int NW, int WL>
 __global__ __launch_bounds__(NW * 64) void k_woq_gemm256(LinearArgs a) {
   using TF = TileFmt<F>;
   static_assert(TF::ARS == 128 && TF::BRS == 128, "128-byte LDS rows");
@@ -432,11 +431,10 @@ __global__ __launch_bounds__(NW * 64) void k_woq_gemm256(LinearArgs a) {
       const int k0 = kt * 64 + part * kpc;
       const bool ok = k0 < K;
       const uint32_t byte0 = (F == KF_BF16) ? 2u * (uint32_t)k0 : (F == KF_FP8 ? (uint32_t)k0 : (uint32_t)k0 / 2u);
-      w[q] = bload128(Wr, off_if(ok, n * wrow + byte0));
-      if constexpr (F == KF_INT4) sc[q] = bload16(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 2u));
-      else if constexpr (F == KF_INT4A) sc[q] = bload32(Sr, off_if(ok, (n * (uint32_t)(K / 128) + (uint32_t)(k0 / 128)) * 4u));
-      else if constexpr (F == KF_NVFP4) sc[q] = bload16(Sr, off_if(ok, n * (uint32_t)(K / 16) + (uint32_t)(k0 / 16)));
-      else if constexpr (F == KF_MXFP4) sc[q] = bload8(Sr, off_if(ok, n * (uint32_t)(K / 32) + (uint32_t)(k0 / 32)));
+      w[q] = bload128(Wr, off_if(ok, w_off<WL>(n, byte0, wrow)));
+      if constexpr (F == KF_INT4 || F == KF_NVFP4) sc[q] = bload16(Sr, off_if(ok, s_off<F, WL>(n, (uint32_t)k0, (uint32_t)K)));
+      else if constexpr (F == KF_INT4A) sc[q] = bload32(Sr, off_if(ok, s_off<F, WL>(n, (uint32_t)k0, (uint32_t)K)));
+      else if constexpr (F == KF_MXFP4) sc[q] = bload8(Sr, off_if(ok, s_off<F, WL>(n, (uint32_t)k0, (uint32_t)K)));
       else sc[q] = 0u;
     }
   };
@@ -550,15 +548,16 @@ struct MxWReg {
   uint32_t sc;    // E8M0 scale byte of the 32-element block
 };
 
+template <int WL>
 __device__ __forceinline__ void mxwreg_load(MxWReg& r, __amdgpu_buffer_rsrc_t Wr, __amdgpu_buffer_rsrc_t Sr, uint32_t n,
                                             int kb, int K) {
   const bool ok = kb < K;
-  const u32x4 v = bload128(Wr, off_if(ok, n * ((uint32_t)K / 2u) + (uint32_t)kb / 2u));
+  const u32x4 v = bload128(Wr, off_if(ok, w_off<WL>(n, (uint32_t)kb / 2u, (uint32_t)K / 2u)));
   r.w[0] = v.x;
   r.w[1] = v.y;
   r.w[2] = v.z;
   r.w[3] = v.w;
-  r.sc = bload8(Sr, off_if(ok, n * (uint32_t)(K / 32) + (uint32_t)(kb / 32)));
+  r.sc = bload8(Sr, off_if(ok, s_off<KF_MXFP4, WL>(n, (uint32_t)kb, (uint32_t)K)));
 }
 
 // LDS slot of 16-byte chunk k (0..15) of activation row r (256-byte rows): the
@@ -566,6 +565,7 @@ __device__ __forceinline__ void mxwreg_load(MxWReg& r, __amdgpu_buffer_rsrc_t Wr
 // 16 distinct 16-byte bank groups
 __device__ __forceinline__ int wreg_pos(int r, int k) { return k ^ ((r & 3) | (((r >> 2) & 1) << 3)); }
 
+template <int WL>
 __global__ __launch_bounds__(512) void k_mx_wreg(LinearArgs a) {
   constexpr int T = 256, TM = 8, TN = 4;
   constexpr int STAGE = T * 256;  // activation rows of one step
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(512) void k_mx_wreg(LinearArgs a) {
   auto loadW = [&](int kt, MxWReg (&r)[TN]) {
 #pragma unroll
     for (int t = 0; t < TN; ++t)
-      mxwreg_load(r[t], Wr, Sr, (uint32_t)(n0 + wn * 64 + 16 * t + c), kt * 128 + 32 * g, K);
+      mxwreg_load<WL>(r[t], Wr, Sr, (uint32_t)(n0 + wn * 64 + 16 * t + c), kt * 128 + 32 * g, K);
   };
 
   uint32_t bias_bits[TN];
@@ -674,13 +674,13 @@ __global__ __launch_bounds__(512) void k_mx_wreg(LinearArgs a) {
   tile_store<128>(a.Y, M, N, m0 + wm * 128, n0 + wn * 64, et, lane);
 }
 
-template <int F, int BM, int BN, int KS, int WGN = 2>
+template <int F, int WL, int BM, int BN, int KS, int WGN = 2>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   constexpr int sm = KS * tile_smem<F, BM, BN>();
   static_assert(sm <= 160 * 1024, "tile exceeds the LDS of a CU");
   static_assert(KS == 1 || (KS - 1) * BM * BN * 4 <= sm, "group partials must fit in the tile buffers");
   static std::atomic<int> done{0};
-  auto k = k_gemm_tiled<F, BM, BN, tile_stages<BM, BN>(), KS, WGN>;
+  auto k = k_gemm_tiled<F, BM, BN, tile_stages<BM, BN>(), KS, WGN, WL>;
   hipError_t e = allow_smem(k, sm, done);
   if (e != hipSuccess) return e;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
@@ -692,7 +692,7 @@ hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
 // registers (128 per wave at four waves per SIMD)
 constexpr int kWoqWaves = 8;
 
-template <int F>
+template <int F, int WL>
 hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   // 256 x 256 and 128 x 128 tiles are planned only when there are enough of
   // them (no K groups); the other shapes run with one or two K groups
@@ -700,7 +700,7 @@ hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t 
     if (p.bm == 256) {
       static std::atomic<int> done{0};
       constexpr int sm = (2 * 256 * 256 > 8 * 128 * kTileRowBytes) ? 2 * 256 * 256 : 8 * 128 * kTileRowBytes;
-      auto k = k_mx_wreg;
+      auto k = k_mx_wreg<WL>;
       hipError_t e = allow_smem(k, sm, done);
       if (e != hipSuccess) return e;
       k<<<dim3((a.N + 255) / 256, (a.M + 255) / 256), 512, sm, s>>>(a);
@@ -710,15 +710,15 @@ hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t 
   if (p.bm == 256) {
     static std::atomic<int> done{0};
     constexpr int sm = (2 * 2 * 256 * 128 > kWoqWaves * 128 * kTileRowBytes) ? 2 * 2 * 256 * 128 : kWoqWaves * 128 * kTileRowBytes;
-    auto k = k_woq_gemm256<F, kWoqWaves>;
+    auto k = k_woq_gemm256<F, kWoqWaves, WL>;
     hipError_t e = allow_smem(k, sm, done);
     if (e != hipSuccess) return e;
     k<<<dim3((a.N + 255) / 256, (a.M + 255) / 256), kWoqWaves * 64, sm, s>>>(a);
     return hipGetLastError();
   }
-  if (p.bm == 128 && p.bn == 128) return launch_tile<F, 128, 128, 1>(a, s);
-  if (p.bm == 128) return p.ks >= 2 ? launch_tile<F, 128, 64, 2>(a, s) : launch_tile<F, 128, 64, 1>(a, s);
-  if (p.bn == 128) return p.ks >= 2 ? launch_tile<F, 64, 128, 2>(a, s) : launch_tile<F, 64, 128, 1>(a, s);
+  if (p.bm == 128 && p.bn == 128) return launch_tile<F, WL, 128, 128, 1>(a, s);
+  if (p.bm == 128) return p.ks >= 2 ? launch_tile<F, WL, 128, 64, 2>(a, s) : launch_tile<F, WL, 128, 64, 1>(a, s);
+  if (p.bn == 128) return p.ks >= 2 ? launch_tile<F, WL, 64, 128, 2>(a, s) : launch_tile<F, WL, 64, 128, 1>(a, s);
   if (p.ks >= 2) {
     // 4-bit weights: four K groups of two waves (32 x 64 outputs each)
     // rather than two groups of four; each activation row is then read from
@@ -727,22 +727,30 @@ hipError_t launch_tiled_f(const LinearArgs& a, const LinearPlan& p, hipStream_t 
     // 22.6 -> 19.7 us, MXFP4 16.2 -> 14.9 and 17.6 -> 16.8 us; FP8 (twice the
     // weight bytes per step) was 1.5-3.4 us slower and keeps two groups.
     constexpr bool four_bit = F == KF_INT4 || F == KF_INT4A || F == KF_NVFP4 || F == KF_MXFP4;
-    if constexpr (four_bit) return launch_tile<F, 64, 64, 4, 1>(a, s);
-    else return launch_tile<F, 64, 64, 2>(a, s);
+    if constexpr (four_bit) return launch_tile<F, WL, 64, 64, 4, 1>(a, s);
+    else return launch_tile<F, WL, 64, 64, 2>(a, s);
   }
-  return launch_tile<F, 64, 64, 1>(a, s);
+  return launch_tile<F, WL, 64, 64, 1>(a, s);
+}
+
+template <int F>
+hipError_t launch_tiled_fl(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if constexpr (F != KF_BF16) {
+    if (a.wl == kLayoutTiles) return launch_tiled_f<F, kLayoutTiles>(a, p, s);
+  }
+  return launch_tiled_f<F, kLayoutRows>(a, p, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_tiled(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   switch (kfmt) {
-    case KF_BF16: return launch_tiled_f<KF_BF16>(a, p, s);
-    case KF_INT4: return launch_tiled_f<KF_INT4>(a, p, s);
-    case KF_INT4A: return launch_tiled_f<KF_INT4A>(a, p, s);
-    case KF_FP8: return launch_tiled_f<KF_FP8>(a, p, s);
-    case KF_NVFP4: return launch_tiled_f<KF_NVFP4>(a, p, s);
-    case KF_MXFP4: return launch_tiled_f<KF_MXFP4>(a, p, s);
+    case KF_BF16: return launch_tiled_fl<KF_BF16>(a, p, s);
+    case KF_INT4: return launch_tiled_fl<KF_INT4>(a, p, s);
+    case KF_INT4A: return launch_tiled_fl<KF_INT4A>(a, p, s);
+    case KF_FP8: return launch_tiled_fl<KF_FP8>(a, p, s);
+    case KF_NVFP4: return launch_tiled_fl<KF_NVFP4>(a, p, s);
+    case KF_MXFP4: return launch_tiled_fl<KF_MXFP4>(a, p, s);
     case KF_FP8S: return launch_f8_gemm_tiled(a, s);
     default: return hipErrorInvalidValue;
   }

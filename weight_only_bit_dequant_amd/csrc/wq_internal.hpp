@@ -2,7 +2,7 @@
 // Launchers assume their arguments were validated by the ABI layer.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -42,6 +42,10 @@ struct LinearPlan {
 
 LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K);
 
+// Packed-weight layouts (the ABI's `layout` argument; see wq_kernel_common.hpp)
+constexpr int kLayoutRows = 0;   // canonical: row n of the packed weight at n * row_bytes
+constexpr int kLayoutTiles = 1;  // tile order: 16 rows x 64 bytes per tile
+
 struct LinearArgs {
   const void* X;         // bf16 [M][K], or E4M3 [M][K] for KF_FP8S
   const void* W;         // packed weight
@@ -53,6 +57,7 @@ struct LinearArgs {
   uint16_t* Y;           // bf16 [M][N]
   float* part;           // split-K partials (workspace)
   int M, N, K;
+  int wl;                // layout of W and its block scales (kLayoutRows / kLayoutTiles)
 };
 
 hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
@@ -62,8 +67,11 @@ hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t N, int64_t K, voi
                            float* gscale, hipStream_t s);
 hipError_t launch_read_stream(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_pack(int fmt, const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
-hipError_t launch_dequantize(int fmt, const void* packed, const void* scales, const float* gscale, int64_t N,
+hipError_t launch_dequantize(int fmt, int wl, const void* packed, const void* scales, const float* gscale, int64_t N,
                              int64_t K, uint16_t* out, hipStream_t s);
+// layout conversion of a packed weight and its block scales (src -> dst layout)
+hipError_t launch_repack(int fmt, int64_t N, int64_t K, int src_wl, const void* src_packed, const void* src_scales,
+                         int dst_wl, void* dst_packed, void* dst_scales, hipStream_t s);
 hipError_t launch_absmax(const uint16_t* X, int64_t numel, float* amax, hipStream_t s);
 hipError_t launch_fp8_scale(const float* amax, float* scale, int64_t count, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* X, int64_t numel, const float* act_scale, uint8_t* Xq,

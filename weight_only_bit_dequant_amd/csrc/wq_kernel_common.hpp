@@ -47,6 +47,42 @@ __device__ __forceinline__ int64_t kbyte(int64_t k) {
   else return k / 2;
 }
 
+// Packed-weight layouts.  kLayoutRows: row n of the packed weight starts at
+// n * row_bytes and the block scales are [N][K / block] row-major.
+// kLayoutTiles (kernel tile order): the weight is cut into tiles of 16 rows x
+// 64 bytes (128 K of a 4-bit format, 64 K of E4M3); tile (n / 16, kb / 64)
+// starts at ((n / 16) * (row_bytes / 64) + kb / 64) * 1024 and holds its 16
+// rows one after the other, so one 16-byte load per lane of a wave reads a
+// whole tile, 1 KiB in 8 full cache lines.  The block scales of each tile
+// follow the same order: SB bytes per row and tile (INT4 2, INT4_ASYM 4,
+// NVFP4 8, MXFP4 4).  The E4M3 row scales and the NVFP4 global scale do not
+// depend on the layout.  Tile order needs N % 16 == 0 and row_bytes % 64 == 0.
+template <int WL>
+__device__ __forceinline__ uint32_t w_off(uint32_t n, uint32_t kb, uint32_t row_bytes) {
+  if constexpr (WL == kLayoutTiles)
+    return ((((n >> 4) * (row_bytes >> 6) + (kb >> 6)) << 10) | ((n & 15u) << 6)) + (kb & 63u);
+  else
+    return n * row_bytes + kb;
+}
+
+// Block-scale geometry of the 4-bit formats: K elements per scale, bytes per scale.
+template <int F>
+struct ScaleT {
+  static constexpr uint32_t BLK = (F == KF_NVFP4) ? 16u : ((F == KF_MXFP4) ? 32u : 128u);
+  static constexpr uint32_t ES = (F == KF_INT4) ? 2u : ((F == KF_INT4A) ? 4u : 1u);
+  static constexpr uint32_t SB = 128u / BLK * ES;  // bytes per row of one 128-K tile
+};
+
+// Byte offset of the block scale that covers K element k of row n.
+template <int F, int WL>
+__device__ __forceinline__ uint32_t s_off(uint32_t n, uint32_t k, uint32_t K) {
+  using S = ScaleT<F>;
+  if constexpr (WL == kLayoutTiles)
+    return (((n >> 4) * (K >> 7) + (k >> 7)) * 16u + (n & 15u)) * S::SB + ((k & 127u) / S::BLK) * S::ES;
+  else
+    return (n * (K / S::BLK) + k / S::BLK) * S::ES;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // INT4: 8 nibbles (K order 0..7) -> bf16 values 136 + code, K order kept.

@@ -90,12 +90,26 @@ constexpr int smem_bytes(bool xlds) {
   return xslots_bytes<F, MT, NTW, NW>(xlds) + NW * (MT * 16 * 16 * NTW) * 4;
 }
 
+// Weights before activations (no-split tiles): every wave issues its packed
+// weight and scale loads, the workgroup meets at a barrier, and only then are
+// the activation loads issued, so that the long-latency weight stream is not
+// queued behind the CU's activation traffic (192 KiB per CU at M = 32,
+// K = 3072).  Measured at N = 4096, K = 3072, M = 32 (cold weights): rows
+// layout INT4 6.52 -> 6.35 us, FP8 7.03 -> 6.57, NVFP4 6.90 -> 6.51, MXFP4
+// 6.55 -> 6.20; in tile order only MXFP4 (5.73 -> 5.65) and NVFP4 (6.08 ->
+// 6.03) gain, while INT4 (5.82 -> 6.01) and FP8 (6.34 -> 6.40) lose.
+template <int F, int WL>
+constexpr bool weights_first() {
+  return WL == kLayoutRows || F == KF_MXFP4 || F == KF_NVFP4;
+}
+
 // K-split plan of one workgroup: NW waves x SPW macro-steps each per block;
 // the S workgroups of a column tile interleave their blocks.
 //
 // Template parameters: F format, MT 16-row tiles, NTW 16-column tiles per wave,
-// NW waves per workgroup, SPW macro-steps whose loads are issued together.
-template <int F, int MT, int NTW, int NW, int SPW, bool XLDS>
+// NW waves per workgroup, SPW macro-steps whose loads are issued together, WL
+// weight layout.
+template <int F, int MT, int NTW, int NW, int SPW, bool XLDS, int WL>
 __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   constexpr int KPL = FmtT<F>::KPL;
   constexpr int MACRO = 4 * KPL;
@@ -149,6 +163,7 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   // once (measured at N = 4096, K = 3072, M = 32: FP8 7.4 -> 7.15-7.25 us,
   // the other formats unchanged; the one/two-row kernel keeps the plain order)
   const int wi = (XLDS && S == 1) ? (wave + (int)(blockIdx.x % NW)) % NW : split * NW + wave;
+  constexpr bool WFB = XLDS && weights_first<F, WL>();
   for (int blk = wi; blk * SPW < T; blk += S * NW) {
     // ---- issue every load of this block before any wait: the activation
     // slices (cache hits; loads return in issue order, so their LDS staging
@@ -195,22 +210,33 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
           // N = 4096, K = 3072, M = 32: INT4 6.7 -> 6.55 us, NVFP4 7.4 -> 7.2,
           // MXFP4 6.8 -> 6.7; FP8 gained nothing at M = 32 and lost 0.3 us at
           // M = 1
+          const uint32_t wo = off_if(kv, w_off<WL>(n, (uint32_t)kbyte<F>(kl), wrow));
           if constexpr (F == KF_INT4 || F == KF_INT4A || F == KF_NVFP4 || F == KF_MXFP4)
-            w[st][t] = bload128_nt(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
+            w[st][t] = bload128_nt(Wr, wo);
           else
-            w[st][t] = bload128(Wr, off_if(kv, n * wrow + (uint32_t)kbyte<F>(kl)));
-          if constexpr (F == KF_INT4) sc[st][t] = bload16(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 2u));
-          else if constexpr (F == KF_INT4A) sc[st][t] = bload32(Sr, off_if(kv, (n * (uint32_t)(K / 128) + (uint32_t)(kl / 128)) * 4u));
-          else if constexpr (F == KF_NVFP4) sc[st][t] = bload16(Sr, off_if(kv, n * (uint32_t)(K / 16) + (uint32_t)(kl / 16)));
-          else if constexpr (F == KF_MXFP4) sc[st][t] = bload8(Sr, off_if(kv, n * (uint32_t)(K / 32) + (uint32_t)(kl / 32)));
-          else sc[st][t] = 0u;
+            w[st][t] = bload128(Wr, wo);
+          // (NVFP4: the lane's 32 K span two 16-K blocks, whose scales are
+          // adjacent bytes in both layouts)
+          if constexpr (F == KF_INT4 || F == KF_NVFP4)
+            sc[st][t] = bload16(Sr, off_if(kv, s_off<F, WL>(n, (uint32_t)kl, (uint32_t)K)));
+          else if constexpr (F == KF_INT4A)
+            sc[st][t] = bload32(Sr, off_if(kv, s_off<F, WL>(n, (uint32_t)kl, (uint32_t)K)));
+          else if constexpr (F == KF_MXFP4)
+            sc[st][t] = bload8(Sr, off_if(kv, s_off<F, WL>(n, (uint32_t)kl, (uint32_t)K)));
+          else
+            sc[st][t] = 0u;
         }
       }
     };
-    // NVFP4 issues its weights first: measured at N = 4096, K = 3072, M = 32,
-    // 7.3-7.4 -> 7.0-7.1 us (unchanged at M = 4 and 64); FP8 and INT4 were
-    // 0.05-0.25 us slower that way, MXFP4 unchanged.
-    if constexpr (F == KF_NVFP4) {
+    if constexpr (WFB) {
+      load_w();
+      __builtin_amdgcn_sched_barrier(0);
+      if (blk == wi) __builtin_amdgcn_s_barrier();  // once per wave (see after the loop)
+      __builtin_amdgcn_sched_barrier(0);
+      load_x();
+    } else if constexpr (F == KF_NVFP4) {
+      // NVFP4 issues its weights first per wave: measured at N = 4096,
+      // K = 3072, M = 32, 7.3-7.4 -> 7.0-7.1 us
       load_w();
       load_x();
     } else {
@@ -326,6 +352,11 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     }
   }
 
+  // a wave without a K block still meets the weights-first barrier once
+  if constexpr (WFB) {
+    if (wi * SPW >= T) __builtin_amdgcn_s_barrier();
+  }
+
   // ---- reduce the wave partials: every wave stores its tile (one 16-byte
   // vector per lane and MFMA tile), then thread tid sums the NW partials of
   // the outputs e = tid + q * NTHR (row-major in the workgroup tile, column
@@ -429,25 +460,25 @@ constexpr int spw_split() {
 
 // 64-column tiles (NTW = 4) run 8 waves of 1.5x the K: at 12 waves their
 // loads and accumulators spilled registers.
-template <int F, int MT, int NTW>
+template <int F, int MT, int NTW, int WL>
 hipError_t launch_nosplit(const LinearArgs& a, dim3 grid, hipStream_t s) {
   constexpr int NW = (NTW == 4) ? 8 : 12;
   constexpr int sm = smem_bytes<F, MT, NTW, NW>(true);
   static_assert(sm <= 160 * 1024, "no-split tile exceeds the LDS of a CU");
   static std::atomic<int> done{0};
-  auto k = k_linear<F, MT, NTW, NW, spw_nosplit<F>() * 12 / NW, true>;
+  auto k = k_linear<F, MT, NTW, NW, spw_nosplit<F>() * 12 / NW, true, WL>;
   hipError_t e = allow_smem(k, sm, done);
   if (e != hipSuccess) return e;
   k<<<grid, NW * 64, sm, s>>>(a, 1);
   return hipGetLastError();
 }
 
-template <int F, int MT>
+template <int F, int MT, int WL>
 hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   dim3 grid(p.gx, p.S, p.gz);
   if (p.cfg == kCfgSplit) {
     constexpr int sm = smem_bytes<F, MT, 4, 4>(false);
-    k_linear<F, MT, 4, 4, spw_split<F>(), false><<<grid, 256, sm, s>>>(a, p.S);
+    k_linear<F, MT, 4, 4, spw_split<F>(), false, WL><<<grid, 256, sm, s>>>(a, p.S);
     if (p.S > 1) k_splitk_reduce<F, MT, 4, 4><<<dim3(p.gx, 1, p.gz), 256, 0, s>>>(a, p.S);
   } else {
     if constexpr (MT == 1) {
@@ -460,135 +491,31 @@ hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
         // cold weights both direct forms take 4.8 us; from four rows up the
         // 12 staged waves win)
         constexpr int sm = smem_bytes<F, MT, 1, 6>(false);
-        k_linear<F, MT, 1, 6, 2 * spw_nosplit<F>(), false><<<grid, 384, sm, s>>>(a, p.S);
+        k_linear<F, MT, 1, 6, 2 * spw_nosplit<F>(), false, WL><<<grid, 384, sm, s>>>(a, p.S);
         return hipGetLastError();
       }
     }
     // no-split tiles with activations staged through LDS
     if constexpr (MT == 2) {
-      if (p.ntw == 2) return launch_nosplit<F, MT, 2>(a, grid, s);
+      if (p.ntw == 2) return launch_nosplit<F, MT, 2, WL>(a, grid, s);
       if constexpr (F != KF_BF16 && F != KF_FP8S) {
-        if (p.ntw == 4) return launch_nosplit<F, MT, 4>(a, grid, s);
+        if (p.ntw == 4) return launch_nosplit<F, MT, 4, WL>(a, grid, s);
       }
     }
-    return launch_nosplit<F, MT, 1>(a, grid, s);
+    return launch_nosplit<F, MT, 1, WL>(a, grid, s);
   }
   return hipGetLastError();
 }
 
 template <int F>
 hipError_t launch_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  return p.mt == 1 ? launch_mt<F, 1>(a, p, s) : launch_mt<F, 2>(a, p, s);
-}
-
-int kpl_of(int kfmt) {
-  switch (kfmt) {
-    case KF_BF16: return 8;
-    case KF_FP8:
-    case KF_FP8S: return 16;
-    default: return 32;
+  if constexpr (F != KF_BF16) {
+    if (a.wl == kLayoutTiles) return p.mt == 1 ? launch_mt<F, 1, kLayoutTiles>(a, p, s) : launch_mt<F, 2, kLayoutTiles>(a, p, s);
   }
-}
-
-int spw_of(int kfmt, int cfg) {
-  const bool b16 = kfmt == KF_BF16, f8 = (kfmt == KF_FP8 || kfmt == KF_FP8S);
-  if (cfg == kCfgSplit) return b16 ? 4 : (f8 ? 2 : 1);
-  return b16 ? 8 : (f8 ? 4 : 2);
+  return p.mt == 1 ? launch_mt<F, 1, kLayoutRows>(a, p, s) : launch_mt<F, 2, kLayoutRows>(a, p, s);
 }
 
 }  // namespace
-
-LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K) {
-  LinearPlan p{};
-  // 65..128 rows of a wide layer (weight-only formats): three or four row
-  // blocks of 64-column tiles (at least 192 workgroups) load everything up
-  // front like the smaller M do, instead of stepping K through LDS tiles.
-  // Measured at N = 4096, K = 3072, M = 72 / 96 / 128: INT4 18.1 -> 12.5 /
-  // 12.6 / 13.2 us, NVFP4 18.4 -> 13.5 / 13.6 / 14.0, MXFP4 15.6 -> 12.3 /
-  // 12.4 / 12.7, FP8 13.9 -> 13.0 / 13.2 / 13.4.
-  const bool wide64 = M > 64 && M <= 128 && kfmt != KF_BF16 && kfmt != KF_FP8S &&
-                      ((N + 63) / 64) * ((M + 31) / 32) >= 192;
-  if (M > 64 && !wide64) {
-    // MFMA-bound: LDS-tiled GEMM; the largest tile that still gives about
-    // 192 workgroups.  (The static FP8 GEMM's tiled kernels choose their own
-    // tiles by the same rule; for it only cfg and the zero workspace matter.)
-    p.cfg = kCfgTiled;
-    p.S = 1;
-    p.bm = 64;
-    p.bn = 64;
-    // 256 x 256 tiles: k_woq_gemm256 (activations loaded straight into LDS);
-    // measured at M = 4096 (N = 4096, K = 3072): INT4 157 -> 114 us against
-    // 128 x 128 tiles, MXFP4 and FP8 on par with the register-staged 256 x 256
-    // kernel it replaced.
-    const int cand[4][2] = {{256, 256}, {128, 128}, {128, 64}, {64, 128}};
-    for (const auto& cb : cand) {
-      const int64_t tiles = ((M + cb[0] - 1) / cb[0]) * ((N + cb[1] - 1) / cb[1]);
-      if (tiles >= 192) {
-        p.bm = cb[0];
-        p.bn = cb[1];
-        break;
-      }
-    }
-    // few tiles: split K over two groups of waves inside each workgroup, so
-    // that each CU runs 8 waves (the K steps are latency-bound otherwise).
-    // Measured at M = 128 and 256 (N = 4096, K = 3072): two groups beat one by
-    // 10-25 %; four groups (64 x 64 tiles only) were slower than two.
-    const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
-    const int64_t steps = (K + 63) / 64;
-    p.ks = 1;
-    if (p.bm < 128 || p.bn < 128) {
-      if (tiles <= 512 && steps >= 16) p.ks = 2;
-    }
-    p.part_bytes = 0;
-    p.ws_bytes = 0;
-    return p;
-  }
-  // 16 or 32 rows per workgroup; 33..64 rows take two row blocks (grid z)
-  // that read the same packed columns, 65..128 three or four.  Workgroup ids of one column tile
-  // differ by gx, so with gx a multiple of 8 both blocks run on the same XCD
-  // (workgroups are dealt to the 8 XCDs round robin) and share its L2 copy.
-  p.mt = M <= 16 ? 1 : 2;
-  p.gz = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
-  // No-split (16 columns x all of K per workgroup) whenever it yields enough
-  // workgroups to cover the chip, or K <= 3072; otherwise 64-column tiles with
-  // K split across workgroups and a second, stream-ordered reduction kernel.
-  // On narrow layers the second launch costs more than the idle CUs: measured
-  // at K = 3072, N = 256 / 512 / 1024, M = 4..64, no-split is 1.2-2.0 us
-  // faster in every format (N = 512, M = 32: FP8 7.6 -> 6.05 us, INT4 7.3 ->
-  // 5.9); at K = 4096 only FP8 gained, and from K = 6144 split wins.
-  const int64_t gx_nosplit = (N + 15) / 16;
-  p.cfg = (gx_nosplit * p.gz >= 128 || K <= 3072) ? kCfgNoSplit : kCfgSplit;
-  const int64_t T = (K + 4 * kpl_of(kfmt) - 1) / (4 * kpl_of(kfmt));
-  if (p.cfg == kCfgSplit) {
-    p.ntw = 4;
-    p.nwaves = 4;
-  } else {
-    // two row blocks (33..64 rows): 32 columns per workgroup when that still
-    // gives 256 workgroups, so that a CU reads one 32-row activation block
-    // (192 KiB at K = 3072) rather than two workgroups' worth; measured at
-    // N = 4096, K = 3072, M = 64: 11.1-12.2 -> 8.6-9.8 us for every format.
-    // (With one row block, 32-column tiles leave half the CUs idle: 1.3-1.8 us
-    // slower at M = 16 and 32.)
-    p.ntw = (p.gz == 2 && ((N + 31) / 32) * p.gz >= 256) ? 2 : 1;
-    if (p.gz >= 3) p.ntw = 4;  // wide64 above
-    p.nwaves = (p.ntw == 4) ? 8 : 12;
-  }
-  p.spw = (p.cfg == kCfgNoSplit) ? spw_of(kfmt, p.cfg) * 12 / p.nwaves : spw_of(kfmt, p.cfg);
-  p.gx = (int)((N + 16 * p.ntw - 1) / (16 * p.ntw));
-  const int64_t base = (int64_t)p.gx * p.gz;
-  int64_t S = 1;
-  if (p.cfg == kCfgSplit) S = (T + (int64_t)p.nwaves * p.spw - 1) / ((int64_t)p.nwaves * p.spw);
-  if (S > kMaxSplit) S = kMaxSplit;  // the waves then loop over several blocks
-  if (S < 1) S = 1;
-  p.S = (int)S;
-  const int64_t E = (int64_t)p.mt * 16 * 16 * p.ntw;
-  const int64_t nthr = 64 * (int64_t)p.nwaves;
-  const int64_t ept = (E + nthr - 1) / nthr;
-  const int64_t slab = nthr * ((ept + 3) / 4) * 16;  // bytes of one workgroup partial
-  p.part_bytes = p.S > 1 ? (size_t)(base * p.S * slab) : 0;
-  p.ws_bytes = p.part_bytes;
-  return p;
-}
 
 hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   if (p.cfg == kCfgTiled) return launch_gemm_tiled(kfmt, a, p, s);

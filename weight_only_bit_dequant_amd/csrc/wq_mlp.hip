@@ -336,11 +336,6 @@ __global__ __launch_bounds__(kWaves * 64) void k_static_mlp2(Mlp2Args a) {
 
 }  // namespace
 
-size_t mlp2_smem_bytes(int64_t K1, int64_t N1, int64_t N2) {
-  return (size_t)16 * (size_t)(((K1 + 255) / 256 * 256 + 16) + ((N1 + 255) / 256 * 256 + 16)) +
-         (size_t)8 * (size_t)(N1 + N2);
-}
-
 hipError_t launch_static_mlp2(const Mlp2Args& a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.M + 15) / 16);
   if (a.K1 <= kSpK1 && a.N1 <= kSpN1 && a.N2 <= kSpN2) {

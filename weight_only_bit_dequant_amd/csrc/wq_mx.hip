@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_mx_quant_act(const uint16_t* __restrict
 // is issued before the first MFMA; out-of-range offsets read zero codes and
 // zero scale bytes, whose products are zero.  Wave partials are reduced
 // through LDS as in the bf16 kernel.
-template <int MT>
+template <int MT, int WL>
 __global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
   constexpr int NW = 12, SPW = 2, NT = 16;
   constexpr int E = MT * 16 * NT;
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
       const int k = (s0 + st) * 128 + 32 * g;  // first K of this lane's block
       const bool kv = k < K;
       const uint32_t n = (uint32_t)(n0 + c);
-      w[st] = bload128(Wr, off_if(kv, n * rowb + (uint32_t)k / 2u));
-      ws[st] = bload8(Wsr, off_if(kv, n * srow + (uint32_t)k / 32u));
+      w[st] = bload128(Wr, off_if(kv, w_off<WL>(n, (uint32_t)k / 2u, rowb)));
+      ws[st] = bload8(Wsr, off_if(kv, s_off<KF_MXFP4, WL>(n, (uint32_t)k, (uint32_t)K)));
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const uint32_t m = (uint32_t)(m0 + 16 * i + c);
@@ -201,7 +201,7 @@ struct MxTile {
 // owns a (BM/2) x (BN/WGN) block.  F8: E4M3 operands (static FP8 path): 128
 // bytes per row and step, no block scales (the MFMA takes 2^0 for both), the
 // epilogue applies act_scale * w_scale[n].
-template <int BM, int BN, int WGN, bool PRE, bool F8>
+template <int BM, int BN, int WGN, bool PRE, bool F8, int WL>
 __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
   constexpr int GT = 128 * WGN, WBN = BN / WGN;
   using TT = MxTile<BM, BN, GT, F8>;
@@ -233,8 +233,9 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
   unsigned char* WS = XS + BM * srow;      //      [BN][srow] weight scale rows
 
   if constexpr (PRE) {
-    // rows m0 .. m0+BM-1 of the scale matrix are one contiguous byte range;
-    // 16-byte chunks, rows past M / N read zero
+    // rows m0 .. m0+BM-1 of the scale matrix are one contiguous byte range
+    // (in tile order too: a 16-row group's scales are consecutive); 16-byte
+    // chunks, rows past M / N read zero
     const int xchunks = BM * (int)srow / 16, wchunks = BN * (int)srow / 16;
     for (int q = tid; q < xchunks; q += GT)
       *reinterpret_cast<u32x4*>(XS + 16 * q) = bload128(Xsr, (uint32_t)m0 * srow + 16u * q);
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
     for (int q = 0; q < TT::NB; ++q) {
       const int id = q * GT + tid, row = id / CPR, part = id % CPR;
       const bool ok = kt * 128 + part * TT::KPC < K;
-      wb[st][q] = bload128(Wr, off_if(ok, (uint32_t)(n0 + row) * rowb + kb + 16u * part));
+      wb[st][q] = bload128(Wr, off_if(ok, w_off<WL>((uint32_t)(n0 + row), kb + 16u * part, rowb)));
     }
     if constexpr (!PRE && !F8) {
       // thread t reads the step's 4 scale bytes of activation row t % BM and
@@ -267,7 +268,8 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
       for (int j = 0; j < 4; ++j) {
         const bool okj = kt * 128 + 32 * j < K;
         xsb[st][j] = bload8(Xsr, off_if(okj, (uint32_t)(m0 + tid % BM) * srow + (uint32_t)kt * 4u + j));
-        wsb[st][j] = bload8(Wsr, off_if(okj, (uint32_t)(n0 + tid % BN) * srow + (uint32_t)kt * 4u + j));
+        wsb[st][j] = bload8(Wsr, off_if(okj, s_off<KF_MXFP4, WL>((uint32_t)(n0 + tid % BN), (uint32_t)(kt * 128 + 32 * j),
+                                                                   (uint32_t)K)));
       }
     }
   };
@@ -355,7 +357,11 @@ __global__ __launch_bounds__(128 * WGN) void k_mx_gemm_tiled(LinearArgs a) {
       for (int t = 0; t < TN; ++t) {
         const int r = wn * WBN + 16 * t + c;
         bf[t] = *reinterpret_cast<const u32x4*>(B + r * TT::ROWB + TT::pos(r, g) * 16);
-        bs[t] = PRE ? ((4 * kt + g < (int)srow) ? WS[r * srow + min(4 * kt + g, (int)srow - 1)] : 127u) : BS[g * BN + r];
+        // (tile order: the copied range holds each 16-row group's 128-K tiles
+        // one after the other, 4 scale bytes per row and tile)
+        const int wsi = (WL == kLayoutTiles) ? (((r >> 4) * ((int)srow >> 2) + min(kt, ((int)srow >> 2) - 1)) * 64 + (r & 15) * 4 + g)
+                                             : r * srow + min(4 * kt + g, (int)srow - 1);
+        bs[t] = PRE ? ((4 * kt + g < (int)srow) ? WS[wsi] : 127u) : BS[g * BN + r];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -426,6 +432,7 @@ __device__ __forceinline__ int f8pos(int r, int k) { return k ^ (((r >> 1) & 1) 
 
 constexpr int kF8Waves = 16;
 
+template <int WL>
 __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // 16 x 16 tiles per wave (WBM x 64 outputs); the first half of the waves
@@ -466,8 +473,8 @@ __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
       const int r = lrow0 + 8 * j + (lane >> 3);
       const int kc = f8pos(r, lane & 7);
       const bool ok = kt * 128 + 16 * kc < K;
-      const uint32_t off =
-          off_if(ok, (lbase + 8u * j + (uint32_t)(lane >> 3)) * (uint32_t)K + (uint32_t)kt * 128u + 16u * kc);
+      const uint32_t row = lbase + 8u * j + (uint32_t)(lane >> 3), kb = (uint32_t)kt * 128u + 16u * kc;
+      const uint32_t off = off_if(ok, loadA ? row * (uint32_t)K + kb : w_off<WL>(row, kb, (uint32_t)K));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(Lr, (__attribute__((address_space(3))) void*)(dst0 + j * 1024), 16, off, 0,
                                                0, 0);
     }
@@ -552,6 +559,7 @@ constexpr int kMxStage = 2 * kMxCodes + 2 * kMxT * 8;  // codes, then scales
 constexpr int kMxColb = (2 * kMxStage > 16 * 64 * kTileRowBytes) ? 2 * kMxStage : 16 * 64 * kTileRowBytes;
 constexpr int kMxSmem = kMxColb + kMxT * 4;  // stages or output tiles, then the tile's biases
 
+template <int WL>
 __global__ __launch_bounds__(1024) void k_mx_gemm256(LinearArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int TM = 2, TN = 2;  // 32 x 32 tiles per wave
@@ -593,13 +601,16 @@ __global__ __launch_bounds__(1024) void k_mx_gemm256(LinearArgs a) {
       const int r = lrow0 + 8 * j + (lane >> 3);
       const int kc = (lane & 7) ^ (r & 7) ^ ((r >> 4) & 1);
       const bool ok = kt * 256 + 32 * kc < K;
-      const uint32_t off = off_if(ok, (lbase + 8u * j + (uint32_t)(lane >> 3)) * rowb + (uint32_t)kt * 128u + 16u * kc);
+      const uint32_t row = lbase + 8u * j + (uint32_t)(lane >> 3), kb = (uint32_t)kt * 128u + 16u * kc;
+      const uint32_t off = off_if(ok, loadA ? row * rowb + kb : w_off<WL>(row, kb, rowb));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(Lr, (__attribute__((address_space(3))) void*)(dst0 + j * 1024), 16, off, 0,
                                                0, 0);
     }
     const int h = lane & 1;
     const bool sok = kt * 8 + 4 * h < (int)srow;
-    const uint32_t soff = off_if(sok, (lbase + (uint32_t)(lane >> 1)) * srow + (uint32_t)kt * 8u + 4u * h);
+    const uint32_t srw = lbase + (uint32_t)(lane >> 1);
+    const uint32_t soff = off_if(sok, loadA ? srw * srow + (uint32_t)kt * 8u + 4u * h
+                                            : s_off<KF_MXFP4, WL>(srw, (uint32_t)(kt * 256 + 128 * h), (uint32_t)K));
     unsigned char* sdst = base + 2 * kMxCodes + (loadA ? 0 : kMxT * 8) + lrow0 * 8;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(Lsr, (__attribute__((address_space(3))) void*)sdst, 4, soff, 0, 0, 0);
   };
@@ -667,7 +678,7 @@ __global__ __launch_bounds__(1024) void k_mx_gemm256(LinearArgs a) {
   tile_store<64>(a.Y, M, N, m0 + wm * 64, n0 + wn * 64, et, lane);
 }
 
-template <int BM, int BN, int WGN = 2>
+template <int BM, int BN, int WL, int WGN = 2>
 hipError_t launch_mx_tile(const LinearArgs& a, hipStream_t s) {
   using TT = MxTile<BM, BN, 128 * WGN, false>;
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
@@ -676,7 +687,7 @@ hipError_t launch_mx_tile(const LinearArgs& a, hipStream_t s) {
   if ((a.K / 32) % 16 == 0 && TT::TILES + pre <= (size_t)limit) {
     static std::atomic<int> done{0};
     const int sm = (int)(TT::TILES + pre);
-    auto k = k_mx_gemm_tiled<BM, BN, WGN, true, false>;
+    auto k = k_mx_gemm_tiled<BM, BN, WGN, true, false, WL>;
     if (sm > 65536 && !done.load(std::memory_order_acquire)) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                          limit);
@@ -686,7 +697,7 @@ hipError_t launch_mx_tile(const LinearArgs& a, hipStream_t s) {
     k<<<grid, 128 * WGN, sm, s>>>(a);
   } else {
     static std::atomic<int> done{0};
-    auto k = k_mx_gemm_tiled<BM, BN, WGN, false, false>;
+    auto k = k_mx_gemm_tiled<BM, BN, WGN, false, false, WL>;
     hipError_t e = allow_smem(k, TT::TILES, done);
     if (e != hipSuccess) return e;
     k<<<grid, 128 * WGN, TT::TILES, s>>>(a);
@@ -694,14 +705,56 @@ hipError_t launch_mx_tile(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGN = 2>
+template <int BM, int BN, int WL, int WGN = 2>
 hipError_t launch_f8_tile(const LinearArgs& a, hipStream_t s) {
   using TT = MxTile<BM, BN, 128 * WGN, true>;
   static std::atomic<int> done{0};
-  auto k = k_mx_gemm_tiled<BM, BN, WGN, false, true>;
+  auto k = k_mx_gemm_tiled<BM, BN, WGN, false, true, WL>;
   hipError_t e = allow_smem(k, TT::TILES, done);
   if (e != hipSuccess) return e;
   k<<<dim3((a.N + BN - 1) / BN, (a.M + BM - 1) / BM), 128 * WGN, TT::TILES, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int WL>
+hipError_t launch_f8_gemm_tiled_l(const LinearArgs& a, hipStream_t s) {
+  // the largest tiles that still give most CUs a workgroup
+  const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if (t256 >= 192) {
+    static std::atomic<int> done{0};
+    hipError_t e = allow_smem(k_f8_gemm256<WL>, kF8Smem, done);
+    if (e != hipSuccess) return e;
+    k_f8_gemm256<WL><<<dim3((a.N + kF8T - 1) / kF8T, (a.M + kF8T - 1) / kF8T), kF8Waves * 64, kF8Smem, s>>>(a);
+    return hipGetLastError();
+  }
+  const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  return t128 >= 192 ? launch_f8_tile<128, 128, WL>(a, s) : launch_f8_tile<64, 64, WL>(a, s);
+}
+
+template <int WL>
+hipError_t launch_mx_linear_l(const LinearArgs& a, hipStream_t s) {
+  if (a.M > 64) {
+    // matrix-core bound: 256 x 256 tiles straight into LDS when they fill the
+    // chip (whole scale dwords per row needed), else 128 x 128 or 64 x 64
+    // through registers
+    const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
+    if (t256 >= 192 && a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.xscales) & 3) == 0 &&
+        (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0) {
+      static std::atomic<int> done{0};
+      hipError_t e = allow_smem(k_mx_gemm256<WL>, kMxSmem, done);
+      if (e != hipSuccess) return e;
+      k_mx_gemm256<WL><<<dim3((a.N + kMxT - 1) / kMxT, (a.M + kMxT - 1) / kMxT), 1024, kMxSmem, s>>>(a);
+      return hipGetLastError();
+    }
+    const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+    return t128 >= 192 ? launch_mx_tile<128, 128, WL>(a, s) : launch_mx_tile<64, 64, WL>(a, s);
+  }
+  const int gx = (a.N + 15) / 16;
+  if (a.M <= 16) {
+    k_mx_linear<1, WL><<<dim3(gx, 1, (a.M + 15) / 16), 768, 0, s>>>(a);
+  } else {
+    k_mx_linear<2, WL><<<dim3(gx, 1, (a.M + 31) / 32), 768, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -714,44 +767,11 @@ hipError_t launch_mx_quantize_act(const uint16_t* X, int64_t M, int64_t K, uint8
 }
 
 hipError_t launch_f8_gemm_tiled(const LinearArgs& a, hipStream_t s) {
-  // the largest tiles that still give most CUs a workgroup
-  const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (t256 >= 192) {
-    static std::atomic<int> done{0};
-    hipError_t e = allow_smem(k_f8_gemm256, kF8Smem, done);
-    if (e != hipSuccess) return e;
-    k_f8_gemm256<<<dim3((a.N + kF8T - 1) / kF8T, (a.M + kF8T - 1) / kF8T), kF8Waves * 64, kF8Smem, s>>>(a);
-    return hipGetLastError();
-  }
-  const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  return t128 >= 192 ? launch_f8_tile<128, 128>(a, s) : launch_f8_tile<64, 64>(a, s);
+  return a.wl == kLayoutTiles ? launch_f8_gemm_tiled_l<kLayoutTiles>(a, s) : launch_f8_gemm_tiled_l<kLayoutRows>(a, s);
 }
 
 hipError_t launch_mx_linear(const LinearArgs& a, hipStream_t s) {
-  if (a.M > 64) {
-    // matrix-core bound: 256 x 256 tiles straight into LDS when they fill the
-    // chip (whole scale dwords per row needed), else 128 x 128 or 64 x 64
-    // through registers
-    const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (t256 >= 192 && a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.xscales) & 3) == 0 &&
-        (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0) {
-      static std::atomic<int> done{0};
-      hipError_t e = allow_smem(k_mx_gemm256, kMxSmem, done);
-      if (e != hipSuccess) return e;
-      k_mx_gemm256<<<dim3((a.N + kMxT - 1) / kMxT, (a.M + kMxT - 1) / kMxT), 1024, kMxSmem, s>>>(a);
-      return hipGetLastError();
-    }
-    const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-
-    return t128 >= 192 ? launch_mx_tile<128, 128>(a, s) : launch_mx_tile<64, 64>(a, s);
-  }
-  const int gx = (a.N + 15) / 16;
-  if (a.M <= 16) {
-    k_mx_linear<1><<<dim3(gx, 1, (a.M + 15) / 16), 768, 0, s>>>(a);
-  } else {
-    k_mx_linear<2><<<dim3(gx, 1, (a.M + 31) / 32), 768, 0, s>>>(a);
-  }
-  return hipGetLastError();
+  return a.wl == kLayoutTiles ? launch_mx_linear_l<kLayoutTiles>(a, s) : launch_mx_linear_l<kLayoutRows>(a, s);
 }
 
 }  // namespace wq

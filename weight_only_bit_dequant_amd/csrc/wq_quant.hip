@@ -5,6 +5,8 @@
 // is built with -fhip-fp32-correctly-rounded-divide-sqrt and without
 // denormal flushing) followed by clamp-then-nearest-even casts, so codes and
 // scales are bit-identical to an IEEE reference.
+#include <type_traits>
+
 #include "wq_device.hpp"
 #include "wq_internal.hpp"
 #include "wq_kernel_common.hpp"
@@ -259,9 +261,16 @@ __global__ __launch_bounds__(kThreads) void k_copy16(const u32x4* __restrict__ s
   if (id < n16) dst[id] = src[id];
 }
 
+__global__ __launch_bounds__(kThreads) void k_copy_bytes(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                         int64_t n) {
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id < n) dst[id] = src[id];
+}
+
 // ---------------------------------------------------------------- dequantize to bf16
-// bf16(fp32(code value * block scale (* global))).  One thread per 8 outputs.
-template <int F>
+// bf16(fp32(code value * block scale (* global))).  One thread per 8 outputs;
+// the packed weight and its block scales are read in layout WL.
+template <int F, int WL>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ P, const void* __restrict__ scales,
                                                       const float* __restrict__ gscale, int64_t N, int64_t K,
                                                       uint16_t* __restrict__ out) {
@@ -269,29 +278,31 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
   const int64_t per_row = K / 8;
   if (id >= N * per_row) return;
   const int64_t n = id / per_row, k0 = (id % per_row) * 8;
+  const unsigned char* S = reinterpret_cast<const unsigned char*>(scales);
   uint16_t r[8];
   if constexpr (F == KF_FP8) {
     const float s = reinterpret_cast<const float*>(scales)[n];
-    const uint8_t* c = P + n * K + k0;
+    const uint8_t* c = P + w_off<WL>((uint32_t)n, (uint32_t)k0, (uint32_t)K);
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = f32_to_bf16(e4m3_decode(c[i]) * s);
   } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(P + n * (K / 2) + k0 / 2);
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(P + w_off<WL>((uint32_t)n, (uint32_t)k0 / 2u, (uint32_t)K / 2u));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t c = (w >> (4 * i)) & 0xFu;
+      const uint32_t so = s_off<F, WL>((uint32_t)n, (uint32_t)(k0 + i), (uint32_t)K);
       float v;
       if constexpr (F == KF_INT4) {
-        const float s = bf16_to_f32(reinterpret_cast<const uint16_t*>(scales)[n * (K / 128) + (k0 + i) / 128]);
+        const float s = bf16_to_f32(*reinterpret_cast<const uint16_t*>(S + so));
         v = (float)((int)c - ((c & 8u) ? 16 : 0)) * s;
       } else if constexpr (F == KF_INT4A) {
-        const uint32_t sw = reinterpret_cast<const uint32_t*>(scales)[n * (K / 128) + (k0 + i) / 128];
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(S + so);
         v = (float)((int)c - (int)((sw >> 16) & 15u)) * bitsf(sw << 16);
       } else if constexpr (F == KF_NVFP4) {
-        const float d = e4m3_decode(reinterpret_cast<const uint8_t*>(scales)[n * (K / 16) + (k0 + i) / 16]);
+        const float d = e4m3_decode(S[so]);
         v = (e2m1_decode(c) * d) * gscale[0];
       } else {  // MXFP4
-        const float p = e8m0_decode(reinterpret_cast<const uint8_t*>(scales)[n * (K / 32) + (k0 + i) / 32]);
+        const float p = e8m0_decode(S[so]);
         v = e2m1_decode(c) * p;
       }
       r[i] = f32_to_bf16(v);
@@ -300,6 +311,54 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
   *reinterpret_cast<u32x4*>(out + n * K + k0) =
       u32x4{r[0] | ((uint32_t)r[1] << 16), r[2] | ((uint32_t)r[3] << 16), r[4] | ((uint32_t)r[5] << 16),
             r[6] | ((uint32_t)r[7] << 16)};
+}
+
+// ---------------------------------------------------------------- layout conversion
+// One thread per 16-byte chunk of packed weight (canonical chunk c = row n,
+// bytes 16 (c % (row_bytes / 16)) ..): copied from its place in layout SRC to
+// its place in layout DST.
+template <int SRC, int DST>
+__global__ __launch_bounds__(kThreads) void k_repack_codes(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                           int64_t N, uint32_t row_bytes) {
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t cpr = row_bytes / 16u;
+  if (id >= N * (int64_t)cpr) return;
+  const uint32_t n = (uint32_t)(id / cpr), kb = (uint32_t)(id % cpr) * 16u;
+  *reinterpret_cast<u32x4*>(dst + w_off<DST>(n, kb, row_bytes)) =
+      *reinterpret_cast<const u32x4*>(src + w_off<SRC>(n, kb, row_bytes));
+}
+
+// One thread per (row, 128-K tile) piece of block scales (ScaleT<F>::SB bytes:
+// 2, 4 or 8, contiguous in both layouts).
+template <int F, int SRC, int DST>
+__global__ __launch_bounds__(kThreads) void k_repack_scales(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                            int64_t N, uint32_t K) {
+  using P = typename std::conditional<ScaleT<F>::SB == 2, uint16_t,
+                                      typename std::conditional<ScaleT<F>::SB == 4, uint32_t, uint64_t>::type>::type;
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t tiles = K / 128u;
+  if (id >= N * (int64_t)tiles) return;
+  const uint32_t n = (uint32_t)(id / tiles), k = (uint32_t)(id % tiles) * 128u;
+  *reinterpret_cast<P*>(dst + s_off<F, DST>(n, k, K)) = *reinterpret_cast<const P*>(src + s_off<F, SRC>(n, k, K));
+}
+
+template <int SRC, int DST>
+hipError_t repack_l(int fmt, int64_t N, int64_t K, const void* sp, const void* ss, void* dp, void* ds, hipStream_t s) {
+  const uint32_t row_bytes = (fmt == KF_FP8) ? (uint32_t)K : (uint32_t)K / 2u;
+  k_repack_codes<SRC, DST><<<grid_for(N * (row_bytes / 16)), kThreads, 0, s>>>((const uint8_t*)sp, (uint8_t*)dp, N,
+                                                                                  row_bytes);
+  const unsigned gs = grid_for(N * (K / 128));
+  const uint8_t* a = (const uint8_t*)ss;
+  uint8_t* b = (uint8_t*)ds;
+  switch (fmt) {
+    case KF_FP8: k_copy_bytes<<<grid_for(N * 4), kThreads, 0, s>>>(a, b, N * 4); break;  // row scales
+    case KF_INT4: k_repack_scales<KF_INT4, SRC, DST><<<gs, kThreads, 0, s>>>(a, b, N, (uint32_t)K); break;
+    case KF_INT4A: k_repack_scales<KF_INT4A, SRC, DST><<<gs, kThreads, 0, s>>>(a, b, N, (uint32_t)K); break;
+    case KF_NVFP4: k_repack_scales<KF_NVFP4, SRC, DST><<<gs, kThreads, 0, s>>>(a, b, N, (uint32_t)K); break;
+    case KF_MXFP4: k_repack_scales<KF_MXFP4, SRC, DST><<<gs, kThreads, 0, s>>>(a, b, N, (uint32_t)K); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- static FP8 helpers
@@ -383,8 +442,9 @@ hipError_t launch_pack(int fmt, const uint8_t* codes, int64_t N, int64_t K, uint
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(int fmt, const void* packed, const void* scales, const float* gscale, int64_t N,
-                             int64_t K, uint16_t* out, hipStream_t s) {
+template <int WL>
+hipError_t dequantize_l(int fmt, const void* packed, const void* scales, const float* gscale, int64_t N, int64_t K,
+                        uint16_t* out, hipStream_t s) {
   const unsigned g = grid_for(N * (K / 8));
   const uint8_t* P = (const uint8_t*)packed;
   switch (fmt) {
@@ -393,14 +453,31 @@ hipError_t launch_dequantize(int fmt, const void* packed, const void* scales, co
       k_copy16<<<grid_for(n16), kThreads, 0, s>>>((const u32x4*)packed, n16, (u32x4*)out);
       break;
     }
-    case KF_INT4: k_dequant<KF_INT4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
-    case KF_INT4A: k_dequant<KF_INT4A><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
-    case KF_FP8: k_dequant<KF_FP8><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
-    case KF_NVFP4: k_dequant<KF_NVFP4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
-    case KF_MXFP4: k_dequant<KF_MXFP4><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_INT4: k_dequant<KF_INT4, WL><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_INT4A: k_dequant<KF_INT4A, WL><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_FP8: k_dequant<KF_FP8, WL><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_NVFP4: k_dequant<KF_NVFP4, WL><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
+    case KF_MXFP4: k_dequant<KF_MXFP4, WL><<<g, kThreads, 0, s>>>(P, scales, gscale, N, K, out); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_dequantize(int fmt, int wl, const void* packed, const void* scales, const float* gscale, int64_t N,
+                             int64_t K, uint16_t* out, hipStream_t s) {
+  return wl == kLayoutTiles ? dequantize_l<kLayoutTiles>(fmt, packed, scales, gscale, N, K, out, s)
+                            : dequantize_l<kLayoutRows>(fmt, packed, scales, gscale, N, K, out, s);
+}
+
+hipError_t launch_repack(int fmt, int64_t N, int64_t K, int src_wl, const void* src_packed, const void* src_scales,
+                         int dst_wl, void* dst_packed, void* dst_scales, hipStream_t s) {
+  if (src_wl == kLayoutRows && dst_wl == kLayoutTiles)
+    return repack_l<kLayoutRows, kLayoutTiles>(fmt, N, K, src_packed, src_scales, dst_packed, dst_scales, s);
+  if (src_wl == kLayoutTiles && dst_wl == kLayoutRows)
+    return repack_l<kLayoutTiles, kLayoutRows>(fmt, N, K, src_packed, src_scales, dst_packed, dst_scales, s);
+  if (src_wl == kLayoutTiles)
+    return repack_l<kLayoutTiles, kLayoutTiles>(fmt, N, K, src_packed, src_scales, dst_packed, dst_scales, s);
+  return repack_l<kLayoutRows, kLayoutRows>(fmt, N, K, src_packed, src_scales, dst_packed, dst_scales, s);
 }
 
 hipError_t launch_absmax(const uint16_t* X, int64_t numel, float* amax, hipStream_t s) {

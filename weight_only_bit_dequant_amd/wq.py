@@ -14,9 +14,12 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libwq.so")
+# WQ_LIB selects another build of the same C ABI (the CPU tests' sanitizer
+# build of the host code); by default the in-tree gfx950 library is loaded.
+LIB_PATH = os.environ.get("WQ_LIB") or os.path.join(HERE, "libwq.so")
 
 FORMATS = {"bf16": 0, "int4": 1, "fp8": 2, "nvfp4": 3, "mxfp4": 4, "int4_asym": 5}
+LAYOUT_ROWS, LAYOUT_TILES = 0, 1
 OK, EINVAL, ESHAPE, EALIGN, EUNSUPPORTED, EWORKSPACE, EHIP = range(7)
 
 
@@ -51,34 +54,36 @@ def lib():
         L.wq_layout.argtypes = [I, I64, I64, SP, SP, SP, SP]
         L.wq_quantize.argtypes = [I, P, I64, I64, P, P, P, P]
         L.wq_pack.argtypes = [I, P, I64, I64, P, P]
-        L.wq_dequantize.argtypes = [I, P, P, P, I64, I64, P, P]
+        I32 = ctypes.c_int32
+        L.wq_dequantize.argtypes = [I, P, I32, P, P, I64, I64, P, P]
+        L.wq_repack.argtypes = [I, I64, I64, I32, P, P, I32, P, P, P]
         L.wq_linear_workspace.argtypes = [I, I64, I64, I64]
         L.wq_linear_workspace.restype = SZ
-        L.wq_linear.argtypes = [I, P, I64, I64, P, P, P, P, I64, P, P, SZ, P]
+        L.wq_linear.argtypes = [I, P, I64, I64, P, I32, P, P, P, I64, P, P, SZ, P]
         L.wq_absmax.argtypes = [P, I64, P, P]
         L.wq_fp8_scale.argtypes = [P, P, I64, P]
         L.wq_fp8_quantize_act.argtypes = [P, I64, I64, P, P, P]
         L.wq_fp8_static_workspace.argtypes = [I64, I64, I64]
         L.wq_fp8_static_workspace.restype = SZ
-        L.wq_fp8_static_linear.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, SZ, P]
+        L.wq_fp8_static_linear.argtypes = [P, I64, I64, P, P, I32, P, P, I64, P, P, SZ, P]
         L.wq_fp8_linear_workspace.argtypes = [I64, I64, I64]
         L.wq_fp8_linear_workspace.restype = SZ
-        L.wq_fp8_linear.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, SZ, P]
+        L.wq_fp8_linear.argtypes = [P, I64, I64, P, P, I32, P, P, I64, P, P, SZ, P]
         L.wq_mx_quantize_act.argtypes = [P, I64, I64, P, P, P]
-        L.wq_mx_linear.argtypes = [P, P, I64, I64, P, P, P, I64, P, P]
+        L.wq_mx_linear.argtypes = [P, P, I64, I64, P, I32, P, P, I64, P, P]
         L.wq_mxfp4_dynamic_workspace.argtypes = [I64, I64]
         L.wq_mxfp4_dynamic_workspace.restype = SZ
-        L.wq_mxfp4_dynamic_linear.argtypes = [P, I64, I64, P, P, P, I64, P, P, SZ, P]
+        L.wq_mxfp4_dynamic_linear.argtypes = [P, I64, I64, P, I32, P, P, I64, P, P, SZ, P]
         L.wq_read_stream.argtypes = [P, SZ, P, P]
         L.wq_fp8_static_mlp2.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, P, P, I64, P, P]
         L.wq_read_stream_words.argtypes = [SZ]
         L.wq_read_stream_words.restype = SZ
-        for name in ("wq_layout", "wq_quantize", "wq_pack", "wq_dequantize", "wq_linear", "wq_absmax",
+        for name in ("wq_layout", "wq_quantize", "wq_pack", "wq_repack", "wq_dequantize", "wq_linear", "wq_absmax",
                      "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear", "wq_fp8_linear",
                      "wq_read_stream", "wq_mx_quantize_act", "wq_mx_linear", "wq_mxfp4_dynamic_linear",
                      "wq_fp8_static_mlp2"):
             getattr(L, name).restype = I
-        if L.wq_abi_version() != 1:
+        if L.wq_abi_version() != 2:
             raise RuntimeError("libwq ABI version mismatch")
         _lib = L
     return _lib
@@ -130,20 +135,25 @@ def wq_pack(fmt, codes, packed):
     _check(lib().wq_pack(_fmt(fmt), _ptr(codes), N, K, _ptr(packed), _stream(codes.device)), "wq_pack")
 
 
-def wq_dequantize(fmt, packed, scales, global_scale, N, K, out):
-    _check(lib().wq_dequantize(_fmt(fmt), _ptr(packed), _ptr(scales), _ptr(global_scale), N, K, _ptr(out),
+def wq_dequantize(fmt, packed, scales, global_scale, N, K, out, layout=LAYOUT_ROWS):
+    _check(lib().wq_dequantize(_fmt(fmt), _ptr(packed), layout, _ptr(scales), _ptr(global_scale), N, K, _ptr(out),
                                _stream(out.device)), "wq_dequantize")
+
+
+def wq_repack(fmt, N, K, src_layout, src_packed, src_scales, dst_layout, dst_packed, dst_scales):
+    _check(lib().wq_repack(_fmt(fmt), N, K, src_layout, _ptr(src_packed), _ptr(src_scales), dst_layout,
+                           _ptr(dst_packed), _ptr(dst_scales), _stream(src_packed.device)), "wq_repack")
 
 
 def wq_linear_workspace(fmt, M, N, K):
     return lib().wq_linear_workspace(_fmt(fmt), M, N, K)
 
 
-def wq_linear(fmt, X, packed, scales, global_scale, bias, N, Y, workspace=None):
+def wq_linear(fmt, X, packed, scales, global_scale, bias, N, Y, workspace=None, layout=LAYOUT_ROWS):
     M, K = X.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().wq_linear(_fmt(fmt), _ptr(X), M, K, _ptr(packed), _ptr(scales), _ptr(global_scale), _ptr(bias),
-                           N, _ptr(Y), _ptr(workspace), ws_bytes, _stream(X.device)), "wq_linear")
+    _check(lib().wq_linear(_fmt(fmt), _ptr(X), M, K, _ptr(packed), layout, _ptr(scales), _ptr(global_scale),
+                           _ptr(bias), N, _ptr(Y), _ptr(workspace), ws_bytes, _stream(X.device)), "wq_linear")
 
 
 def wq_absmax(X, amax):
@@ -164,12 +174,12 @@ def wq_fp8_static_workspace(M, N, K):
     return lib().wq_fp8_static_workspace(M, N, K)
 
 
-def wq_fp8_static_linear(X, act_scale, Wq, w_scale, bias, Y, workspace):
+def wq_fp8_static_linear(X, act_scale, Wq, w_scale, bias, Y, workspace, layout=LAYOUT_ROWS):
     M, K = X.shape
     N = Wq.shape[0]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().wq_fp8_static_linear(_ptr(X), M, K, _ptr(act_scale), _ptr(Wq), _ptr(w_scale), _ptr(bias), N,
-                                      _ptr(Y), _ptr(workspace), ws_bytes, _stream(X.device)),
+    _check(lib().wq_fp8_static_linear(_ptr(X), M, K, _ptr(act_scale), _ptr(Wq), layout, _ptr(w_scale), _ptr(bias),
+                                      N, _ptr(Y), _ptr(workspace), ws_bytes, _stream(X.device)),
            "wq_fp8_static_linear")
 
 
@@ -177,12 +187,12 @@ def wq_fp8_linear_workspace(M, N, K):
     return lib().wq_fp8_linear_workspace(M, N, K)
 
 
-def wq_fp8_linear(Xq, act_scale, Wq, w_scale, bias, Y, workspace=None):
+def wq_fp8_linear(Xq, act_scale, Wq, w_scale, bias, Y, workspace=None, layout=LAYOUT_ROWS):
     M, K = Xq.shape
     N = Wq.shape[0]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().wq_fp8_linear(_ptr(Xq), M, K, _ptr(act_scale), _ptr(Wq), _ptr(w_scale), _ptr(bias), N, _ptr(Y),
-                               _ptr(workspace), ws_bytes, _stream(Xq.device)), "wq_fp8_linear")
+    _check(lib().wq_fp8_linear(_ptr(Xq), M, K, _ptr(act_scale), _ptr(Wq), layout, _ptr(w_scale), _ptr(bias), N,
+                               _ptr(Y), _ptr(workspace), ws_bytes, _stream(Xq.device)), "wq_fp8_linear")
 
 
 def wq_mx_quantize_act(X, Xq, Xs):
@@ -190,9 +200,9 @@ def wq_mx_quantize_act(X, Xq, Xs):
     _check(lib().wq_mx_quantize_act(_ptr(X), M, K, _ptr(Xq), _ptr(Xs), _stream(X.device)), "wq_mx_quantize_act")
 
 
-def wq_mx_linear(Xq, Xs, K, Wq, Ws, bias, N, Y):
+def wq_mx_linear(Xq, Xs, K, Wq, Ws, bias, N, Y, layout=LAYOUT_ROWS):
     M = Xq.shape[0]
-    _check(lib().wq_mx_linear(_ptr(Xq), _ptr(Xs), M, K, _ptr(Wq), _ptr(Ws), _ptr(bias), N, _ptr(Y),
+    _check(lib().wq_mx_linear(_ptr(Xq), _ptr(Xs), M, K, _ptr(Wq), layout, _ptr(Ws), _ptr(bias), N, _ptr(Y),
                               _stream(Xq.device)), "wq_mx_linear")
 
 
@@ -200,10 +210,10 @@ def wq_mxfp4_dynamic_workspace(M, K):
     return lib().wq_mxfp4_dynamic_workspace(M, K)
 
 
-def wq_mxfp4_dynamic_linear(X, Wq, Ws, bias, N, Y, workspace):
+def wq_mxfp4_dynamic_linear(X, Wq, Ws, bias, N, Y, workspace, layout=LAYOUT_ROWS):
     M, K = X.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().wq_mxfp4_dynamic_linear(_ptr(X), M, K, _ptr(Wq), _ptr(Ws), _ptr(bias), N, _ptr(Y),
+    _check(lib().wq_mxfp4_dynamic_linear(_ptr(X), M, K, _ptr(Wq), layout, _ptr(Ws), _ptr(bias), N, _ptr(Y),
                                          _ptr(workspace), ws_bytes, _stream(X.device)), "wq_mxfp4_dynamic_linear")
 
 
@@ -231,14 +241,16 @@ _WS = {}
 
 def workspace(nbytes, device):
     """A uint8 workspace of at least `nbytes`, cached per (device, stream).
-    It holds split-K partials, which need no initialisation, so it is reused."""
+    It holds split-K partials and quantized activations, which need no
+    initialisation, so it is reused."""
     if nbytes == 0:
         return None
     dev = torch.device(device)
     key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     t = _WS.get(key)
     if t is None or t.numel() < nbytes:
-        torch.cuda.current_stream(dev).synchronize()
+        # the caching allocator keeps a freed buffer for this stream until the
+        # work queued on it has run, so growing needs no host synchronization
         t = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _WS[key] = t
     return t
@@ -259,9 +271,11 @@ def scale_dtype_shape(fmt, N, K):
     return None, None
 
 
-def quantize(fmt, W):
+def quantize(fmt, W, layout=LAYOUT_ROWS):
     """Quantize bf16 W[N, K] on its device and pack it.  Returns a dict with
-    codes (one per byte), packed, scales and global (NVFP4) tensors."""
+    codes (one per byte), packed, scales and global (NVFP4) tensors; with
+    ``layout=LAYOUT_TILES`` the packed weight and scales are then converted to
+    the kernel tile order (``wq_repack``) and the dict's ``layout`` says so."""
     f = _fmt(fmt)
     N, K = W.shape
     dev = W.device
@@ -273,12 +287,23 @@ def quantize(fmt, W):
     _, pb, _, _ = wq_layout(f, N, K)
     packed = torch.empty(pb, dtype=torch.uint8, device=dev).view(N, pb // N if N else 0)
     wq_pack(f, codes, packed)
-    return {"fmt": f, "N": N, "K": K, "codes": codes, "packed": packed, "scales": scales, "global": g}
+    q = {"fmt": f, "N": N, "K": K, "codes": codes, "packed": packed, "scales": scales, "global": g,
+         "layout": LAYOUT_ROWS}
+    return repack(q, layout) if layout != LAYOUT_ROWS else q
+
+
+def repack(q, layout):
+    """A copy of quantize result `q` with its packed weight and scales in `layout`."""
+    if q.get("layout", LAYOUT_ROWS) == layout:
+        return q
+    packed, scales = torch.empty_like(q["packed"]), torch.empty_like(q["scales"])
+    wq_repack(q["fmt"], q["N"], q["K"], q.get("layout", LAYOUT_ROWS), q["packed"], q["scales"], layout, packed, scales)
+    return dict(q, packed=packed, scales=scales, layout=layout)
 
 
 def dequantize(q):
     out = torch.empty((q["N"], q["K"]), dtype=torch.bfloat16, device=q["packed"].device)
-    wq_dequantize(q["fmt"], q["packed"], q["scales"], q["global"], q["N"], q["K"], out)
+    wq_dequantize(q["fmt"], q["packed"], q["scales"], q["global"], q["N"], q["K"], out, q.get("layout", LAYOUT_ROWS))
     return out
 
 
@@ -291,23 +316,24 @@ def linear(X, q, bias=None, out=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     ws = workspace(wq_linear_workspace(q["fmt"], M, N, K), X.device)
-    wq_linear(q["fmt"], X, q["packed"], q["scales"], q["global"], bias, N, out, ws)
+    wq_linear(q["fmt"], X, q["packed"], q["scales"], q["global"], bias, N, out, ws, q.get("layout", LAYOUT_ROWS))
     return out
 
 
 def dense(W):
     """Wrap a bf16 weight as the unquantized format (for ``linear``)."""
     N, K = W.shape
-    return {"fmt": 0, "N": N, "K": K, "codes": None, "packed": W, "scales": None, "global": None}
+    return {"fmt": 0, "N": N, "K": K, "codes": None, "packed": W, "scales": None, "global": None,
+            "layout": LAYOUT_ROWS}
 
 
-def static_fp8_linear(X, act_scale, Wq, w_scale, bias=None, out=None):
+def static_fp8_linear(X, act_scale, Wq, w_scale, bias=None, out=None, layout=LAYOUT_ROWS):
     M, K = X.shape
     N = Wq.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     ws = workspace(wq_fp8_static_workspace(M, N, K), X.device)
-    wq_fp8_static_linear(X, act_scale, Wq, w_scale, bias, out, ws)
+    wq_fp8_static_linear(X, act_scale, Wq, w_scale, bias, out, ws, layout)
     return out
 
 
@@ -328,7 +354,7 @@ def mxfp4_dynamic_linear(X, q, bias=None, out=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     ws = workspace(wq_mxfp4_dynamic_workspace(M, K), X.device)
-    wq_mxfp4_dynamic_linear(X, q["packed"], q["scales"], bias, N, out, ws)
+    wq_mxfp4_dynamic_linear(X, q["packed"], q["scales"], bias, N, out, ws, q.get("layout", LAYOUT_ROWS))
     return out
 
 
