@@ -4,7 +4,9 @@
 One step = one pass of the whole hot path over one batch X[32, 3072] (bf16):
 the four weight-only dequant-GEMMs (INT4 group-128, FP8 per-row, NVFP4, MXFP4;
 each y = x . deq(W)^T + b, bf16 out) and the static-FP8 Linear (activation Q to
-E4M3, then the FP8 GEMM).  Weights stay packed in HBM; every launch reads a
+E4M3, then the FP8 GEMM).  Weights stay packed in HBM in the library's kernel
+tile order (layout 1, made once by wq_repack; the canonical rows layout is
+timed beside it per format); every launch reads a
 different copy of the packed weight + scales (copies per format total
 >= 512 MiB, twice the 256 MB Infinity Cache), so the weight stream is cold.  X
 and bias stay warm (they are the previous layer's output).
@@ -194,6 +196,9 @@ def cpu_baseline(seconds_per_format=3.0):
 # ------------------------------------------------------------------ GPU timing
 
 
+LAYOUT = 1  # the packed weights' layout in the step: kernel tile order
+
+
 def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
     """The other workload points, reported beside the M=32 line: MXFP4 at
     M in {1, 32, 256, 4096}, the static-FP8 layer at M=4096 and the MXFP4
@@ -224,11 +229,11 @@ def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
                 for i in range(first, first + count):
                     r = lay["reps"][i % len(lay["reps"])]
                     if fmt == "static_fp8":
-                        wq.wq_fp8_static_linear(X, lay["act_scale"], r["packed"], r["scales"], None, Y, ws)
+                        wq.wq_fp8_static_linear(X, lay["act_scale"], r["packed"], r["scales"], None, Y, ws, LAYOUT)
                     elif fmt == "mxfp4_dynamic":
-                        wq.wq_mxfp4_dynamic_linear(X, r["packed"], r["scales"], lay["bias"], N, Y, ws)
+                        wq.wq_mxfp4_dynamic_linear(X, r["packed"], r["scales"], lay["bias"], N, Y, ws, LAYOUT)
                     else:
-                        wq.wq_linear("mxfp4", X, r["packed"], r["scales"], None, lay["bias"], N, Y, ws)
+                        wq.wq_linear("mxfp4", X, r["packed"], r["scales"], None, lay["bias"], N, Y, ws, LAYOUT)
 
             reps = reps_small if Mv <= 256 else reps_large
             g = capture(run, reps)
@@ -315,14 +320,20 @@ def main_bench(args):
         info = synth.WORKLOADS[fmt]
         W, b, X = synth.linear_case(N, K, M, cfg=info["cfg"], bias=info["bias"])
         qfmt = "fp8" if fmt == "static_fp8" else fmt
-        q = wq.quantize(qfmt, synth.as_torch_bf16(W, dev))
+        q0 = wq.quantize(qfmt, synth.as_torch_bf16(W, dev))
+        q = wq.repack(q0, LAYOUT)
         eff = effective_bytes(fmt)
         copies = max(2, -(-COLD_BYTES // eff))
         reps = [{"packed": q["packed"], "scales": q["scales"], "global": q["global"]}]
         for _ in range(copies - 1):
             reps.append({"packed": q["packed"].clone(), "scales": q["scales"].clone(),
                          "global": None if q["global"] is None else q["global"].clone()})
-        lay = {"reps": reps, "X": synth.as_torch_bf16(X, dev),
+        # the same weights in the canonical rows layout (the comparison graphs)
+        rows = [{"packed": q0["packed"], "scales": q0["scales"], "global": q0["global"]}]
+        for _ in range(copies - 1):
+            rows.append({"packed": q0["packed"].clone(), "scales": q0["scales"].clone(),
+                         "global": None if q0["global"] is None else q0["global"].clone()})
+        lay = {"reps": reps, "rows": rows, "X": synth.as_torch_bf16(X, dev),
                "bias": synth.as_torch_bf16(b, dev) if b is not None else None,
                "Y": torch.empty((M, N), dtype=torch.bfloat16, device=dev), "fmt": qfmt}
         if fmt == "static_fp8":
@@ -347,17 +358,20 @@ def main_bench(args):
     sink = torch.zeros(wq.wq_read_stream_words(STREAM_POOL), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
-    def launch(name, i, hot=False):
+    def launch(name, i, hot=False, rows=False):
         lay = layers["static_fp8" if name.startswith("static") else name]
-        r = lay["reps"][0 if hot else i % len(lay["reps"])]
+        pool = lay["rows"] if rows else lay["reps"]
+        lo = 0 if rows else LAYOUT
+        r = pool[0 if hot else i % len(pool)]
         if name == "static_fp8":
-            wq.wq_fp8_static_linear(lay["X"], lay["act_scale"], r["packed"], r["scales"], lay["bias"], lay["Y"], ws)
+            wq.wq_fp8_static_linear(lay["X"], lay["act_scale"], r["packed"], r["scales"], lay["bias"], lay["Y"], ws,
+                                    lo)
         elif name == "static_q":
             wq.wq_fp8_quantize_act(lay["X"], lay["act_scale"], lay["Xq"])
         elif name == "static_gemm":
-            wq.wq_fp8_linear(lay["Xq"], lay["act_scale"], r["packed"], r["scales"], lay["bias"], lay["Y"], ws)
+            wq.wq_fp8_linear(lay["Xq"], lay["act_scale"], r["packed"], r["scales"], lay["bias"], lay["Y"], ws, lo)
         else:
-            wq.wq_linear(lay["fmt"], lay["X"], r["packed"], r["scales"], r["global"], lay["bias"], N, lay["Y"], ws)
+            wq.wq_linear(lay["fmt"], lay["X"], r["packed"], r["scales"], r["global"], lay["bias"], N, lay["Y"], ws, lo)
 
     def stream_launch(fmt, i):
         size = -(-effective_bytes(fmt) // 256) * 256
@@ -391,6 +405,8 @@ def main_bench(args):
         parts.append(("stream_" + f, capture(lambda a, c, f=f: [stream_launch(f, i) for i in range(a, a + c)], Kst)))
     for f in ([] if args.no_hot else FORMATS):
         parts.append(("hot_" + f, capture(lambda a, c, f=f: [launch(f, i, hot=True) for i in range(a, a + c)], Kst)))
+    for k in ([] if args.no_hot else FORMATS + ["static_gemm"]):
+        parts.append(("rows_" + k, capture(lambda a, c, k=k: [launch(k, i, rows=True) for i in range(a, a + c)], Kst)))
     g_warm = capture(steps_fn, max(1, args.warmup))
     g_warm.replay()
     for _, g in parts[1:]:
@@ -425,6 +441,8 @@ def main_bench(args):
             d["copies"] = len(layers[k]["reps"])
             if "hot_" + k in us:
                 d["hot_us_per_launch"] = round(us["hot_" + k], 3)
+        if "rows_" + k in us:
+            d["rows_layout_us_per_launch"] = round(us["rows_" + k], 3)
         if k == "static_gemm":
             d["copies"] = len(layers["static_fp8"]["reps"])
         if k in traffic:
@@ -471,7 +489,8 @@ def main_bench(args):
         "data": "synthetic",
         "config": {"workload": "nn.Linear(3072->4096) bf16+bias, M=32: INT4-g128 / FP8-row / NVFP4 / MXFP4 "
                                "weight-only dequant-GEMMs + static-FP8 (act Q + FP8 GEMM), cold weight copies",
-                   "M": M, "N": N, "K": K, "formats": STEP, "cold": True},
+                   "M": M, "N": N, "K": K, "formats": STEP, "cold": True,
+                   "weight_layout": "kernel tile order (layout 1)" if LAYOUT == 1 else "rows (layout 0)"},
         "roofline": roofline,
         "per_format": per_format,
         "per_kernel": per_kernel,

@@ -218,6 +218,25 @@ wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* pa
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two-kernel form of the same Linear ("TorchAO FP8 Weight-Only
+ * Quantization (Linear)", intro: where the DQ is not fused into the GEMM, DQ
+ * and GEMM run as two kernels): wq_dequantize writes the bf16 weight into the
+ * workspace, then the dense bf16 GEMM computes
+ * Y = bf16(X . W_bf16^T (+ bias)) with fp32 accumulation.  The weight is
+ * rounded to bf16 before the product (the wq_dequantize value), so results
+ * differ from wq_linear's by that rounding: FP8 row scales and the NVFP4
+ * global scale, which wq_linear applies exactly in its epilogue, and INT4
+ * group scales enter through bf16(code * scale).  Same arguments as
+ * wq_linear; the workspace holds the N*K bf16 weight (and the dense GEMM's
+ * split-K partials): wq_linear_dq_gemm_workspace bytes.  Both launches are
+ * checked before the first is enqueued.
+ */
+size_t wq_linear_dq_gemm_workspace(int fmt, int64_t M, int64_t N, int64_t K);
+wq_status wq_linear_dq_gemm(int fmt, const void* X, int64_t M, int64_t K, const void* packed, int32_t layout,
+                            const void* scales, const float* global_scale, const void* bias, int64_t N, void* Y,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Calibration observer ("TorchAO Static FP8 Quantization (Linear)", "Calibrate,
  * then insert static FP8 Q/DQ": per-tensor activation min/max over the
  * calibration forwards, read symmetrically): amax = max(amax, max|X|) over

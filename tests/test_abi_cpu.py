@@ -211,3 +211,19 @@ def test_layout_validation():
     assert L.wq_repack(1, 0, 256, 0, None, None, 1, None, None, None) == wq.OK
     assert L.wq_fp8_linear(v(16), 4, 96, v(16), v(16), 1, v(16), None, 16, v(16), None, 0, None) == wq.EUNSUPPORTED
     assert L.wq_mx_linear(v(16), v(16), 4, 96, v(16), 1, v(16), None, 64, v(16), None) == wq.EUNSUPPORTED
+
+
+def test_two_kernel_form_validation():
+    L = wq.lib()
+    v = ctypes.c_void_p
+    need = wq.wq_linear_dq_gemm_workspace("mxfp4", 32, 4096, 3072)
+    assert need >= 4096 * 3072 * 2
+    assert wq.wq_linear_dq_gemm_workspace("bf16", 32, 64, 64) == 0
+    call = lambda fmt=4, M=32, K=3072, N=4096, ws=256, wsb=need, layout=0, X=16: L.wq_linear_dq_gemm(
+        fmt, v(X), M, K, v(16), layout, v(16), None, None, N, v(16), v(ws), wsb, None)
+    assert call(fmt=0) == wq.EINVAL  # nothing to dequantize
+    assert call(K=48) == wq.ESHAPE
+    assert call(wsb=need - 1) == wq.EWORKSPACE
+    assert call(X=8) == wq.EALIGN
+    assert call(layout=1, K=96) == wq.EUNSUPPORTED  # tiles need K % 128
+    assert call(M=0) == wq.OK

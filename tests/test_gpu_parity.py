@@ -182,11 +182,17 @@ def test_linear_wide_64_column_tiles(fmt, N, M):
 
 
 @pytest.mark.parametrize("fmt,N", [("int4", 200), ("fp8", 200), ("nvfp4", 208), ("mxfp4", 224), ("int4_asym", 200)])
-def test_linear_ragged_n(fmt, N):
-    # column tail that does not fill the 64-column workgroup tile
-    W, b, X = synth.linear_case(N, 256, 5, cfg=33)
+@pytest.mark.parametrize("K", [256, 4096])
+@pytest.mark.parametrize("M", [2, 5, 40])
+def test_linear_ragged_n(fmt, N, K, M):
+    # A narrow layer with a column tail.  K = 256 runs the no-split tiles (16
+    # columns per workgroup: INT4 and FP8 at N = 200 end in a half tile); K =
+    # 4096 splits K across workgroups of 64 columns and sums them in the
+    # reduction kernel, where every N here ends in a partial tile (N % 64 =
+    # 8, 16, 32).  M = 2 and 5 take one row block, M = 40 two.
+    W, b, X = synth.linear_case(N, K, M, cfg=33)
     _, Y = run_linear(fmt, W, b, X)
-    assert_close(Y, oracle_linear(fmt, W, b, X), f"{fmt} ragged N={N}")
+    assert_close(Y, oracle_linear(fmt, W, b, X), f"{fmt} ragged N={N} K={K} M={M}")
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -294,6 +294,47 @@ wq_status wq_linear(int fmt, const void* X, int64_t M, int64_t K, const void* pa
                        workspace, workspace_bytes, stream);
 }
 
+// Two-kernel form: [dense GEMM split-K partials][bf16 W, N*K*2]
+static size_t dq_gemm_w_offset(int64_t M, int64_t N, int64_t K) {
+  return align256(wq::plan_linear(wq::KF_BF16, M, N, K).ws_bytes);
+}
+
+size_t wq_linear_dq_gemm_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (!valid_fmt(fmt) || fmt == WQ_BF16 || M <= 0 || N <= 0 || K <= 0) return 0;
+  return dq_gemm_w_offset(M, N, K) + align256((size_t)N * (size_t)K * 2);
+}
+
+wq_status wq_linear_dq_gemm(int fmt, const void* X, int64_t M, int64_t K, const void* packed, int32_t layout,
+                            const void* scales, const float* global_scale, const void* bias, int64_t N, void* Y,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_fmt(fmt) || fmt == WQ_BF16) return fail(WQ_EINVAL, "wq_linear_dq_gemm: unsupported format %d", fmt);
+  // the quantized weight's own checks (shape rule, layout, pointers), as the fused call makes them
+  wq::LinearArgs qa;
+  wq::LinearPlan qp;
+  bool empty;
+  wq_status st = linear_check(kfmt_of(fmt), fmt, X, M, K, packed, layout, scales, global_scale, nullptr, bias, N, Y,
+                              nullptr, 0, &qa, &qp, &empty);
+  if (st == WQ_EWORKSPACE) st = WQ_OK;  // the fused kernel's split-K needs do not apply here
+  if (st != WQ_OK || empty) return st;
+  const size_t need = wq_linear_dq_gemm_workspace(fmt, M, N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(WQ_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(WQ_EALIGN, "workspace must be 16-byte aligned");
+  if (2 * N * K >= kMaxBufferBytes) return fail(WQ_EUNSUPPORTED, "bf16 weight of 2^31 bytes or more");
+  // the dense GEMM on the dequantized weight, checked before anything is enqueued
+  void* wd = (char*)workspace + dq_gemm_w_offset(M, N, K);
+  wq::LinearArgs a;
+  wq::LinearPlan p;
+  st = linear_check(wq::KF_BF16, WQ_BF16, X, M, K, wd, WQ_LAYOUT_ROWS, nullptr, nullptr, nullptr, bias, N, Y,
+                    workspace, workspace_bytes, &a, &p, &empty);
+  if (st != WQ_OK || empty) return st;
+  st = hip_status(wq::launch_dequantize(kfmt_of(fmt), layout, packed, scales, global_scale, N, K, (uint16_t*)wd,
+                                        (hipStream_t)stream),
+                  "wq_linear_dq_gemm dequantize launch");
+  if (st != WQ_OK) return st;
+  return hip_status(wq::launch_linear(wq::KF_BF16, a, p, (hipStream_t)stream), "wq_linear_dq_gemm GEMM launch");
+}
+
 wq_status wq_absmax(const void* X, int64_t numel, float* amax, void* stream) {
   if (numel < 0) return fail(WQ_EINVAL, "negative numel");
   if (numel == 0) return ok();

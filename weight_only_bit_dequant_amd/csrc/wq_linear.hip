@@ -6,10 +6,12 @@
 // GEMM while activations stay bf16 (NVFP4 adds a two-level block x global
 // scale).  The static-FP8 page's intro runs the GEMM itself in FP8.  Here:
 //
-//  * no-split tiles (wide layers): one workgroup = 12 waves = 16 output
-//    columns (32 for two row blocks) x all of K; each wave owns a contiguous
-//    K range (split-K inside the workgroup).  Split tiles (narrow layers): 4 waves = 64 columns x a K
-//    range, with the K ranges of one column tile spread over S workgroups;
+//  * no-split tiles (whenever they give at least 128 workgroups, and at any
+//    width for K <= 3072): one workgroup = 12 waves = 16 output columns (32
+//    for two row blocks) x all of K; each wave owns a contiguous K range
+//    (split-K inside the workgroup).  Split tiles (narrow layers with
+//    K > 3072): 4 waves = 64 columns x a K range, with the K ranges of one
+//    column tile spread over S workgroups;
 //  * each wave issues every load of its K range (activations, packed weights
 //    and block scales; bias and column scale at the start) before the first
 //    wait, as buffer loads whose out-of-range offsets read

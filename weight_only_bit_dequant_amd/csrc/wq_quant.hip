@@ -503,10 +503,18 @@ hipError_t launch_quantize_act(const uint16_t* X, int64_t numel, const float* ac
 }
 
 // Read-only stream (measurement aid): workgroup b reads the 16 KiB block b
-// (1024 chunks of 16 bytes, four per thread, all issued before the first use)
-// and stores the XOR of its 32-bit words to sink[b].  Offsets past the end
-// read zero (neutral for XOR).  One plain store per workgroup: no atomics on a
-// shared address, which would serialize the workgroups.
+// (1024 chunks of 16 bytes, four per thread, all issued before the first use,
+// non-temporal like the 4-bit weight loads) and stores the XOR of its 32-bit
+// words to sink[b].  Offsets past the end read zero (neutral for XOR).  One
+// plain store per workgroup: no atomics on a shared address, which would
+// serialize the workgroups.  Of thirteen variants measured as graphs of 200
+// launches over cold copies (256 to 3076 workgroups of 256 to 1024 threads,
+// 1 to 16 loads per thread in flight, with and without non-temporal loads;
+// the best of three replays): this form was fastest at both sizes, 3.06 us
+// for 6.68 MB and 3.83 us for 12.6 MB; with ordinary loads 3.30 and 4.10 us;
+// grids of about one workgroup per CU (102-272 workgroups of 256-1024
+// threads, 3-16 loads per thread) 3.27-3.64 us and 4.10-4.21 us; an empty
+// kernel in the same graph 1.6 us.
 namespace {
 __global__ __launch_bounds__(256) void k_read_stream(const void* p, uint32_t bytes, uint32_t* sink) {
   __shared__ uint32_t part[4];
@@ -514,7 +522,7 @@ __global__ __launch_bounds__(256) void k_read_stream(const void* p, uint32_t byt
   const uint32_t base = (uint32_t)blockIdx.x * 1024u + threadIdx.x;
   u32x4 v[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = bload128(r, (base + 256u * q) * 16u);
+  for (int q = 0; q < 4; ++q) v[q] = bload128_nt(r, (base + 256u * q) * 16u);
   uint32_t h = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) h ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;

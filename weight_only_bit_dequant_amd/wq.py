@@ -60,6 +60,9 @@ def lib():
         L.wq_linear_workspace.argtypes = [I, I64, I64, I64]
         L.wq_linear_workspace.restype = SZ
         L.wq_linear.argtypes = [I, P, I64, I64, P, I32, P, P, P, I64, P, P, SZ, P]
+        L.wq_linear_dq_gemm_workspace.argtypes = [I, I64, I64, I64]
+        L.wq_linear_dq_gemm_workspace.restype = SZ
+        L.wq_linear_dq_gemm.argtypes = [I, P, I64, I64, P, I32, P, P, P, I64, P, P, SZ, P]
         L.wq_absmax.argtypes = [P, I64, P, P]
         L.wq_fp8_scale.argtypes = [P, P, I64, P]
         L.wq_fp8_quantize_act.argtypes = [P, I64, I64, P, P, P]
@@ -78,8 +81,10 @@ def lib():
         L.wq_fp8_static_mlp2.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, P, P, I64, P, P]
         L.wq_read_stream_words.argtypes = [SZ]
         L.wq_read_stream_words.restype = SZ
-        for name in ("wq_layout", "wq_quantize", "wq_pack", "wq_repack", "wq_dequantize", "wq_linear", "wq_absmax",
-                     "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear", "wq_fp8_linear",
+        for name in ("wq_layout", "wq_quantize", "wq_pack", "wq_repack", "wq_dequantize", "wq_linear",
+                     "wq_linear_dq_gemm", "wq_absmax",
+                     "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear",
+                     "wq_fp8_linear",
                      "wq_read_stream", "wq_mx_quantize_act", "wq_mx_linear", "wq_mxfp4_dynamic_linear",
                      "wq_fp8_static_mlp2"):
             getattr(L, name).restype = I
@@ -154,6 +159,18 @@ def wq_linear(fmt, X, packed, scales, global_scale, bias, N, Y, workspace=None, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().wq_linear(_fmt(fmt), _ptr(X), M, K, _ptr(packed), layout, _ptr(scales), _ptr(global_scale),
                            _ptr(bias), N, _ptr(Y), _ptr(workspace), ws_bytes, _stream(X.device)), "wq_linear")
+
+
+def wq_linear_dq_gemm_workspace(fmt, M, N, K):
+    return lib().wq_linear_dq_gemm_workspace(_fmt(fmt), M, N, K)
+
+
+def wq_linear_dq_gemm(fmt, X, packed, scales, global_scale, bias, N, Y, workspace, layout=LAYOUT_ROWS):
+    M, K = X.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().wq_linear_dq_gemm(_fmt(fmt), _ptr(X), M, K, _ptr(packed), layout, _ptr(scales), _ptr(global_scale),
+                                   _ptr(bias), N, _ptr(Y), _ptr(workspace), ws_bytes, _stream(X.device)),
+           "wq_linear_dq_gemm")
 
 
 def wq_absmax(X, amax):
@@ -317,6 +334,19 @@ def linear(X, q, bias=None, out=None):
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     ws = workspace(wq_linear_workspace(q["fmt"], M, N, K), X.device)
     wq_linear(q["fmt"], X, q["packed"], q["scales"], q["global"], bias, N, out, ws, q.get("layout", LAYOUT_ROWS))
+    return out
+
+
+def linear_two_kernel(X, q, bias=None, out=None):
+    """The two-kernel form (``wq_linear_dq_gemm``): dequantize to bf16, then the
+    dense bf16 GEMM."""
+    M, K = X.shape
+    N = q["N"]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    ws = workspace(wq_linear_dq_gemm_workspace(q["fmt"], M, N, K), X.device)
+    wq_linear_dq_gemm(q["fmt"], X, q["packed"], q["scales"], q["global"], bias, N, out, ws,
+                      q.get("layout", LAYOUT_ROWS))
     return out
 
 
