@@ -275,6 +275,22 @@ wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float*
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * wq_fp8_static_linear without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The quantized activations and split-K partials go
+ * to a scratch array of 16 MiB that the library holds on each GPU it runs on
+ * until the process ends: wq_fp8_static_workspace(M, N, K) must not exceed
+ * 16 MiB (M * K up to about 16 Mi elements; WQ_EUNSUPPORTED otherwise).  The
+ * call allocates nothing.  Every call on a GPU shares that GPU's scratch, so
+ * calls that overlap on one GPU (different streams, or threads without
+ * ordering) race and must be serialized by the caller.  The scratch needs no
+ * initialisation.  Same arguments and results as wq_fp8_static_linear.
+ */
+wq_status wq_fp8_static_linear_noalloc(const void* X, int64_t M, int64_t K, const float* act_scale, const void* Wq,
+                                       int32_t layout, const float* w_scale, const void* bias, int64_t N, void* Y,
+                                       void* stream);
+
+/*
  * The FP8 x FP8 GEMM of the static path on activations that are already
  * quantized (same page, "Graph after export": the Q node's E4M3 output and the
  * E4M3 weight each pass a DQ into the linear; intro: that pair runs as one FP8

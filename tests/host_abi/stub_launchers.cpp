@@ -42,4 +42,5 @@ hipError_t launch_static_mlp2(const Mlp2Args&, hipStream_t) { return attempt(); 
 hipError_t launch_mx_quantize_act(const uint16_t*, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t) { return attempt(); }
 hipError_t launch_mx_linear(const LinearArgs&, hipStream_t) { return attempt(); }
 hipError_t launch_f8_gemm_tiled(const LinearArgs&, hipStream_t) { return attempt(); }
+hipError_t noalloc_scratch(void**) { return attempt(); }
 }  // namespace wq

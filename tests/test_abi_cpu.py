@@ -213,6 +213,23 @@ def test_layout_validation():
     assert L.wq_mx_linear(v(16), v(16), 4, 96, v(16), 1, v(16), None, 64, v(16), None) == wq.EUNSUPPORTED
 
 
+def test_noalloc_static_linear_limits():
+    """The allocation-free static-FP8 Linear rejects problems whose scratch
+    would exceed its fixed 16 MiB before touching HIP."""
+    L = wq.lib()
+    v = ctypes.c_void_p
+    before = _launch_attempts()
+    # M * K = 32 Mi activations: E4M3 copy alone is 32 MiB
+    assert L.wq_fp8_static_linear_noalloc(v(16), 4096, 8192, v(16), v(16), 0, v(16), None, 4096, v(16),
+                                          None) == wq.EUNSUPPORTED
+    assert b"16777216" in L.wq_last_error()
+    assert L.wq_fp8_static_linear_noalloc(v(16), 4, 24, v(16), v(16), 0, v(16), None, 16, v(16), None) == \
+        wq.EUNSUPPORTED  # K % 16
+    assert L.wq_fp8_static_linear_noalloc(v(16), 0, 32, v(16), v(16), 0, v(16), None, 16, v(16), None) == wq.OK
+    assert L.wq_fp8_static_linear_noalloc(v(16), -1, 32, v(16), v(16), 0, v(16), None, 16, v(16), None) == wq.EINVAL
+    assert _launch_attempts() == before
+
+
 def test_two_kernel_form_validation():
     L = wq.lib()
     v = ctypes.c_void_p

@@ -402,6 +402,24 @@ wq_status wq_fp8_static_linear(const void* X, int64_t M, int64_t K, const float*
   return hip_status(wq::launch_linear(wq::KF_FP8S, a, p, (hipStream_t)stream), "wq_linear launch");
 }
 
+wq_status wq_fp8_static_linear_noalloc(const void* X, int64_t M, int64_t K, const float* act_scale, const void* Wq,
+                                       int32_t layout, const float* w_scale, const void* bias, int64_t N, void* Y,
+                                       void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(WQ_EINVAL, "negative size");
+  if (M == 0 || N == 0) return ok();
+  if (K > 0 && K % 16) return fail(WQ_EUNSUPPORTED, "static FP8 linear needs K %% 16 == 0 (K=%lld)", (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WQ_EUNSUPPORTED, "dimension above 2^30");
+  const size_t need = wq_fp8_static_workspace(M, N, K);
+  if (need > wq::kNoAllocScratchBytes)
+    return fail(WQ_EUNSUPPORTED, "wq_fp8_static_linear_noalloc: needs %zu scratch bytes, the limit is %zu", need,
+                wq::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  wq_status st = hip_status(wq::noalloc_scratch(&scratch), "wq_fp8_static_linear_noalloc scratch");
+  if (st != WQ_OK) return st;
+  return wq_fp8_static_linear(X, M, K, act_scale, Wq, layout, w_scale, bias, N, Y, scratch,
+                              wq::kNoAllocScratchBytes, stream);
+}
+
 size_t wq_fp8_linear_workspace(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   return wq::plan_linear(wq::KF_FP8S, M, N, K).ws_bytes;

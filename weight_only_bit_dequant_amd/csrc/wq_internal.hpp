@@ -61,6 +61,11 @@ struct LinearArgs {
 };
 
 hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
+
+// Scratch of the allocation-free static-FP8 Linear: a device array of this
+// size per GPU; noalloc_scratch gives its address on the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_gemm_tiled(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
 
 hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t N, int64_t K, void* codes, void* scales,

@@ -69,6 +69,7 @@ def lib():
         L.wq_fp8_static_workspace.argtypes = [I64, I64, I64]
         L.wq_fp8_static_workspace.restype = SZ
         L.wq_fp8_static_linear.argtypes = [P, I64, I64, P, P, I32, P, P, I64, P, P, SZ, P]
+        L.wq_fp8_static_linear_noalloc.argtypes = [P, I64, I64, P, P, I32, P, P, I64, P, P]
         L.wq_fp8_linear_workspace.argtypes = [I64, I64, I64]
         L.wq_fp8_linear_workspace.restype = SZ
         L.wq_fp8_linear.argtypes = [P, I64, I64, P, P, I32, P, P, I64, P, P, SZ, P]
@@ -83,7 +84,7 @@ def lib():
         L.wq_read_stream_words.restype = SZ
         for name in ("wq_layout", "wq_quantize", "wq_pack", "wq_repack", "wq_dequantize", "wq_linear",
                      "wq_linear_dq_gemm", "wq_absmax",
-                     "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear",
+                     "wq_fp8_scale", "wq_fp8_quantize_act", "wq_fp8_static_linear", "wq_fp8_static_linear_noalloc",
                      "wq_fp8_linear",
                      "wq_read_stream", "wq_mx_quantize_act", "wq_mx_linear", "wq_mxfp4_dynamic_linear",
                      "wq_fp8_static_mlp2"):
@@ -198,6 +199,14 @@ def wq_fp8_static_linear(X, act_scale, Wq, w_scale, bias, Y, workspace, layout=L
     _check(lib().wq_fp8_static_linear(_ptr(X), M, K, _ptr(act_scale), _ptr(Wq), layout, _ptr(w_scale), _ptr(bias),
                                       N, _ptr(Y), _ptr(workspace), ws_bytes, _stream(X.device)),
            "wq_fp8_static_linear")
+
+
+def wq_fp8_static_linear_noalloc(X, act_scale, Wq, w_scale, bias, Y, layout=LAYOUT_ROWS):
+    M, K = X.shape
+    N = Wq.shape[0]
+    _check(lib().wq_fp8_static_linear_noalloc(_ptr(X), M, K, _ptr(act_scale), _ptr(Wq), layout, _ptr(w_scale),
+                                              _ptr(bias), N, _ptr(Y), _stream(X.device)),
+           "wq_fp8_static_linear_noalloc")
 
 
 def wq_fp8_linear_workspace(M, N, K):
