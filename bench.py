@@ -108,7 +108,8 @@ def algorithmic_bytes(name):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))):
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")) +
+                    glob.glob(os.path.join(CSRC, "*.cpp"))):
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
@@ -510,10 +511,13 @@ KERNEL_LABELS = {1: "int4", 2: "fp8", 3: "nvfp4", 4: "mxfp4", 5: "static_gemm"}
 
 
 def label_of(name):
-    """Step label of a kernel name in an M=32 run (`--no-sweep`), else None."""
-    m = re.search(r"k_linear<(\d+), ", name)
+    """Step label of a kernel name in an M=32 run (`--no-sweep`), else None;
+    small-M kernels reading the rows layout (the comparison graphs) get a
+    "rows_" prefix."""
+    m = re.search(r"k_linear<(\d+), [^>]*?, (\d+)>", name)
     if m:
-        return KERNEL_LABELS.get(int(m.group(1)))
+        lab = KERNEL_LABELS.get(int(m.group(1)))
+        return lab if lab is None or int(m.group(2)) == LAYOUT else "rows_" + lab
     if "k_quant_act" in name:
         return "static_q"
     if "k_read_stream" in name:
@@ -574,7 +578,7 @@ def counters_summary(fetch_dir, write_dir, cmd):
         scaled = kib * 1024.0 * cal[cname]
         lab = label_of(name)
         lines.append("| `%s` | %s | %s | %d | %.1f | %.0f |" % (_short(name, 70), lab or "", cname, len(xs), kib, scaled))
-        if lab and lab != "stream":
+        if lab and lab != "stream" and not lab.startswith("rows_"):
             per.setdefault(lab, 0.0)
             per[lab] += scaled
     rec = {"src_sha256": kernel_source_hash(), "calibration": {k: round(v, 4) for k, v in cal.items()},

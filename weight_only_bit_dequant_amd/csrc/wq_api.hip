@@ -253,7 +253,7 @@ static wq_status linear_check(int kfmt, int fmt, const void* X, int64_t M, int64
   if (kfmt != wq::KF_NVFP4 && gscale) return fail(WQ_EINVAL, "global_scale must be NULL for %s", fmt_name(fmt));
   if (kfmt == wq::KF_FP8S && !act_scale) return fail(WQ_EINVAL, "null act_scale");
   if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return fail(WQ_EALIGN, "X, weight and Y must be 16-byte aligned");
-  *p = wq::plan_linear(kfmt, M, N, K);
+  *p = wq::plan_linear(kfmt, M, N, K, layout);
   if (p->ws_bytes > 0) {
     if (!ws || ws_bytes < p->ws_bytes)
       return fail(WQ_EWORKSPACE, "workspace of %zu bytes required (got %zu)", p->ws_bytes, ws ? ws_bytes : (size_t)0);

@@ -27,6 +27,10 @@ constexpr int kCfgSplit = 0;
 constexpr int kCfgNoSplit = 1;
 constexpr int kCfgTiled = 2;
 
+// Packed-weight layouts (the ABI's `layout` argument; see wq_kernel_common.hpp)
+constexpr int kLayoutRows = 0;   // canonical: row n of the packed weight at n * row_bytes
+constexpr int kLayoutTiles = 1;  // tile order: 16 rows x 64 bytes per tile
+
 struct LinearPlan {
   int cfg;        // kCfgSplit or kCfgNoSplit
   int mt;         // 16-row MFMA tiles per workgroup (1 or 2)
@@ -40,11 +44,10 @@ struct LinearPlan {
   size_t part_bytes, ws_bytes;  // split-K partials (0 without a split)
 };
 
-LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K);
+// `wl` (the weight layout) picks among tile shapes of the same workspace
+// needs: the workspace size never depends on it.
+LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K, int wl = kLayoutRows);
 
-// Packed-weight layouts (the ABI's `layout` argument; see wq_kernel_common.hpp)
-constexpr int kLayoutRows = 0;   // canonical: row n of the packed weight at n * row_bytes
-constexpr int kLayoutTiles = 1;  // tile order: 16 rows x 64 bytes per tile
 
 struct LinearArgs {
   const void* X;         // bf16 [M][K], or E4M3 [M][K] for KF_FP8S

@@ -100,9 +100,14 @@ constexpr int smem_bytes(bool xlds) {
 // layout INT4 6.52 -> 6.35 us, FP8 7.03 -> 6.57, NVFP4 6.90 -> 6.51, MXFP4
 // 6.55 -> 6.20; in tile order only MXFP4 (5.73 -> 5.65) and NVFP4 (6.08 ->
 // 6.03) gain, while INT4 (5.82 -> 6.01) and FP8 (6.34 -> 6.40) lose.
-template <int F, int WL>
+template <int F, int WL, int MT, int NTW>
 constexpr bool weights_first() {
-  return WL == kLayoutRows || F == KF_MXFP4 || F == KF_NVFP4;
+  if constexpr (WL == kLayoutRows) return true;
+  // tile order with 16-row blocks of 32-column tiles (17..32 rows), measured
+  // at N = 4096, K = 3072, M = 32 without -> with: MXFP4 5.42 -> 5.26 us,
+  // FP8 6.15 -> 6.06 us, INT4 5.39 -> 5.71 us (INT4_ASYM follows INT4)
+  else if constexpr (MT == 1 && NTW == 2) return F == KF_MXFP4 || F == KF_FP8;
+  else return F == KF_MXFP4 || F == KF_NVFP4;
 }
 
 // K-split plan of one workgroup: NW waves x SPW macro-steps each per block;
@@ -164,8 +169,9 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   // CUs of an XCD do not all request the same activation and weight lines at
   // once (measured at N = 4096, K = 3072, M = 32: FP8 7.4 -> 7.15-7.25 us,
   // the other formats unchanged; the one/two-row kernel keeps the plain order)
-  const int wi = (XLDS && S == 1) ? (wave + (int)(blockIdx.x % NW)) % NW : split * NW + wave;
-  constexpr bool WFB = XLDS && weights_first<F, WL>();
+  const int rot = (XLDS && S == 1) ? (int)(blockIdx.x % NW) : 0;  // K-block rotation of the waves
+  const int wi = (XLDS && S == 1) ? (wave + rot) % NW : split * NW + wave;
+  constexpr bool WFB = XLDS && weights_first<F, WL, MT, NTW>();
   for (int blk = wi; blk * SPW < T; blk += S * NW) {
     // ---- issue every load of this block before any wait: the activation
     // slices (cache hits; loads return in issue order, so their LDS staging
@@ -362,7 +368,9 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   // ---- reduce the wave partials: every wave stores its tile (one 16-byte
   // vector per lane and MFMA tile), then thread tid sums the NW partials of
   // the outputs e = tid + q * NTHR (row-major in the workgroup tile, column
-  // n0 + tid % NT) in wave order.
+  // n0 + tid % NT) in the order of their K blocks (wave (j - rot) mod NW holds
+  // block j), so that every tile configuration with the same K blocks per
+  // wave adds the same partials in the same order and gives the same bits.
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     float sum = 0.f;
     if (e < E) {
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) sum += red[w2 * E + idx];
+      for (int j = 0; j < NW; ++j) sum += red[((j + NW - rot) % NW) * E + idx];
     }
     v[q] = sum;
   }
@@ -498,6 +506,9 @@ hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
       }
     }
     // no-split tiles with activations staged through LDS
+    if constexpr (MT == 1 && WL == kLayoutTiles && (F == KF_INT4 || F == KF_INT4A || F == KF_MXFP4 || F == KF_FP8)) {
+      if (p.ntw == 2) return launch_nosplit<F, MT, 2, WL>(a, grid, s);
+    }
     if constexpr (MT == 2) {
       if (p.ntw == 2) return launch_nosplit<F, MT, 2, WL>(a, grid, s);
       if constexpr (F != KF_BF16 && F != KF_FP8S) {
