@@ -208,7 +208,7 @@ size_t wq_linear_workspace(int fmt, int64_t M, int64_t N, int64_t K);
  * Numerics by M: up to 128 rows (the small-M kernels) INT4 groups are summed
  * exactly as s * (sum_k x_k (code_k + 136) - 136 sum_k x_k) in fp32 (the
  * INT4_ASYM bias is 128 + zero-point), i.e. the scale multiplies the group's
- * fp32 partial sum; above that (the LDS-tiled kernels) each INT4 weight is
+ * fp32 partial sum; above that (the mid-M and LDS-tiled kernels) each INT4 weight is
  * first rounded to bf16(code * s) -- the wq_dequantize value -- and then
  * multiplied.  The other formats' decoded weights are exact in bf16 at every
  * M, so only the accumulation order differs.

@@ -26,6 +26,7 @@ extern "C" const char* hipGetErrorString(hipError_t e) { return e == hipSuccess 
 namespace wq {
 hipError_t launch_linear(int, const LinearArgs&, const LinearPlan&, hipStream_t) { return attempt(); }
 hipError_t launch_gemm_tiled(int, const LinearArgs&, const LinearPlan&, hipStream_t) { return attempt(); }
+hipError_t launch_gemm_mid(int, const LinearArgs&, hipStream_t) { return attempt(); }
 hipError_t launch_quantize(int, const uint16_t*, int64_t, int64_t, void*, void*, float*, hipStream_t) { return attempt(); }
 hipError_t launch_read_stream(const void*, size_t, uint32_t*, hipStream_t) { return attempt(); }
 hipError_t launch_pack(int, const uint8_t*, int64_t, int64_t, uint8_t*, hipStream_t) { return attempt(); }

@@ -23,16 +23,20 @@ constexpr int kMaxSplit = 8;  // K splits across workgroups of one column tile
 //  kCfgNoSplit : 16 columns x 12 waves per workgroup covering all of K
 //  kCfgTiled   : LDS-tiled GEMM for larger M (BM x BN tiles, weights decoded
 //                once per tile)
+//  kCfgMid     : 64 x 64 tiles of 8 waves that split K, weights in registers,
+//                activations loaded straight into LDS (wq_gemm_mid.hip)
 constexpr int kCfgSplit = 0;
 constexpr int kCfgNoSplit = 1;
 constexpr int kCfgTiled = 2;
+constexpr int kCfgMid = 3;
+constexpr int64_t kMidMaxK = 16384;  // K limit of the mid-M kernel (16 K blocks per wave)
 
 // Packed-weight layouts (the ABI's `layout` argument; see wq_kernel_common.hpp)
 constexpr int kLayoutRows = 0;   // canonical: row n of the packed weight at n * row_bytes
 constexpr int kLayoutTiles = 1;  // tile order: 16 rows x 64 bytes per tile
 
 struct LinearPlan {
-  int cfg;        // kCfgSplit or kCfgNoSplit
+  int cfg;        // kCfgSplit, kCfgNoSplit, kCfgTiled or kCfgMid
   int mt;         // 16-row MFMA tiles per workgroup (1 or 2)
   int ntw;        // 16-column tiles per wave (= per workgroup)
   int nwaves;     // waves per workgroup
@@ -70,6 +74,7 @@ hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hip
 constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_gemm_tiled(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
+hipError_t launch_gemm_mid(int kfmt, const LinearArgs& a, hipStream_t s);
 
 hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t N, int64_t K, void* codes, void* scales,
                            float* gscale, hipStream_t s);

@@ -532,6 +532,7 @@ hipError_t launch_f(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
 
 hipError_t launch_linear(int kfmt, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   if (p.cfg == kCfgTiled) return launch_gemm_tiled(kfmt, a, p, s);
+  if (p.cfg == kCfgMid) return launch_gemm_mid(kfmt, a, s);
   switch (kfmt) {
     case KF_BF16: return launch_f<KF_BF16>(a, p, s);
     case KF_INT4: return launch_f<KF_INT4>(a, p, s);

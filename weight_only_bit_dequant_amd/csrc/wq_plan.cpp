@@ -36,6 +36,27 @@ LinearPlan plan_linear(int kfmt, int64_t M, int64_t N, int64_t K, int wl) {
   // 12.4 / 12.7, FP8 13.9 -> 13.0 / 13.2 / 13.4.
   const bool wide64 = M > 64 && M <= 128 && kfmt != KF_BF16 && kfmt != KF_FP8S &&
                       ((N + 63) / 64) * ((M + 31) / 32) >= 192;
+  // 129 rows and more, up to three rounds of 64 x 64 tiles on the chip: the
+  // mid-M kernel (8 waves split K inside the workgroup, no barrier per K
+  // step).  Measured against the LDS-tiled kernels (graphs, cold weights):
+  // N = 4096, K = 3072, M = 160 / 256 / 512 / 768: MXFP4 15.8 / 15.9 / 23.0 /
+  // 34.0 -> 10.7 / 10.7 / 19.8 / 28.6 us, INT4 17.3 / 18.0 / 28.9 / 44.2 ->
+  // 13.5 / 14.0 / 26.2 / 38.0; N = 512 .. 2048, K = 1024 .. 4096, M = 160 ..
+  // 512: 13-38 % faster in every case.  At 1024 tiles (M = 1024 at N = 4096,
+  // M = 512 at N = 8192) the 128 x 128 tiles win by 5-30 %.  The kernel needs
+  // K % 128 == 0; with fewer than 8 K blocks some of its waves would idle.
+  const bool mid_fmt = kfmt == KF_INT4 || kfmt == KF_INT4A || kfmt == KF_FP8 || kfmt == KF_NVFP4 || kfmt == KF_MXFP4;
+  if (mid_fmt && M > 128 && K % 128 == 0 && K >= 1024 && K <= kMidMaxK &&
+      ((M + 63) / 64) * ((N + 63) / 64) <= 768) {
+    p.cfg = kCfgMid;
+    p.S = 1;
+    p.bm = 64;
+    p.bn = 64;
+    p.ks = 1;
+    p.part_bytes = 0;
+    p.ws_bytes = 0;
+    return p;
+  }
   if (M > 64 && !wide64) {
     // MFMA-bound: LDS-tiled GEMM; the largest tile that still gives about
     // 192 workgroups.  (The static FP8 GEMM's tiled kernels choose their own
