@@ -2,7 +2,8 @@
 that every launch configuration of the dequant-GEMM is hit with ragged edges:
 the one/two-row kernel, the 16- and 32-row no-split kernels (16- and
 32-column tiles), the split-K path with its reduction kernel, and the tiled
-kernels (64x64 with two or four K groups, 128x64, 64x128, 128x128).  Outputs
+kernels (64x64 with two or four K groups, 128x64, 64x128, 128x128) and the
+mid-M kernel (129+ rows, 64x64 tiles whose waves split K).  Outputs
 are compared with the oracle's fp64 result on the dequantized weight at the
 same bar as the other parity tests (relative Frobenius error 1e-2)."""
 
@@ -37,17 +38,22 @@ REGIMES = [
     ((65, 200), (64, 512), (128, 896)),       # 64x64 tiles, one group
     ((900, 1100), (1536, 2600), (256, 1280)),  # 128x64 tiles
     ((1500, 2100), (2048, 3000), (128, 512)),  # 128x128 tiles
+    # mid-M kernel (129+ rows, up to 768 tiles of 64x64): K drawn as a
+    # multiple of 128 so that the plan can take it
+    ((129, 700), (256, 4160), (1024, 4096), 128),
 ]
 # WQ_SWEEP_SEED / WQ_SWEEP_PER_REGIME draw a different or larger sweep (the
 # default is the committed one)
 CASES = []
 _PER = int(os.environ.get("WQ_SWEEP_PER_REGIME", "3"))
 _rng = np.random.RandomState(int(os.environ.get("WQ_SWEEP_SEED", "20261203")))
-for _i, (_mr, _nr, _kr) in enumerate(REGIMES):
+for _i, _reg in enumerate(REGIMES):
+    _mr, _nr, _kr = _reg[:3]
+    _kmul = _reg[3] if len(_reg) > 3 else 1
     for _j in range(_PER):
         _fmt = FMTS[(3 * _i + _j) % len(FMTS)]
         CASES.append((_fmt, int(_rng.randint(_mr[0], _mr[1] + 1)), int(_rng.randint(_nr[0], _nr[1] + 1)),
-                      int(_rng.randint(_kr[0], _kr[1] + 1)), 600 + _PER * _i + _j))
+                      int(_rng.randint(_kr[0], _kr[1] + 1)) // _kmul * _kmul, 600 + _PER * _i + _j))
 
 
 def _round(fmt, N, K):
