@@ -180,6 +180,11 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   const int rot = (XLDS && S == 1) ? (int)(blockIdx.x % NW) : 0;  // K-block rotation of the waves
   const int wi = (XLDS && S == 1) ? (wave + rot) % NW : split * NW + wave;
   constexpr bool WFB = XLDS && weights_first<F, WL, MT, NTW>();
+  // early weight decode: weights-first tiles of the 4-bit float formats whose
+  // decoded weights fit beside the activations in registers (16 or 32 rows x
+  // one or two 16-column tiles, two K steps; with two row tiles and two column
+  // tiles it spilled 13-27 registers)
+  constexpr bool EDW = WFB && (F == KF_NVFP4 || F == KF_MXFP4) && SPW * NTW * MT <= 4;
   for (int blk = wi; blk * SPW < T; blk += S * NW) {
     // ---- issue every load of this block before any wait: the activation
     // slices (cache hits; loads return in issue order, so their LDS staging
@@ -266,6 +271,27 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     // of the ~20 loads of a wave outstanding at a time.
     __builtin_amdgcn_sched_barrier(0);
 
+    // Early decode (EDW): the weights were issued before the activations and
+    // land first, so the 4-bit float formats decode them while the activation
+    // loads are still in flight.  Same values, same MFMA order.  Measured at
+    // N = 4096, K = 3072, M = 32: NVFP4 6.14-6.28 -> 6.07-6.17 us, MXFP4 5.29
+    // -> 5.11 us.
+    bf16x8 bw[EDW ? SPW : 1][EDW ? NTW : 1][EDW ? 4 : 1];
+    if constexpr (EDW) {
+#pragma unroll
+      for (int st = 0; st < SPW; ++st)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (F == KF_NVFP4)
+              bw[st][t][j] = dec_fp4_mul(w[st][t][j], e4m3_decode((sc[st][t] >> (ssh + (j < 2 ? 0u : 8u))) & 0xFFu));
+            else
+              bw[st][t][j] = dec_fp4_pow2(w[st][t][j], e8m0_decode((sc[st][t] >> ssh) & 0xFFu));
+          }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
     // ---- decode and multiply
 #pragma unroll
     for (int st = 0; st < SPW; ++st) {
@@ -324,7 +350,10 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
         for (int j = 0; j < 4; ++j) {
           bf16x8 b[NTW];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) b[t] = dec_fp4_mul(w[st][t][j], e4m3_decode((sc[st][t] >> (ssh + (j < 2 ? 0u : 8u))) & 0xFFu));
+          for (int t = 0; t < NTW; ++t) {
+            if constexpr (EDW) b[t] = bw[st][t][j];
+            else b[t] = dec_fp4_mul(w[st][t][j], e4m3_decode((sc[st][t] >> (ssh + (j < 2 ? 0u : 8u))) & 0xFFu));
+          }
 #pragma unroll
           for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -335,7 +364,10 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
         for (int j = 0; j < 4; ++j) {
           bf16x8 b[NTW];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) b[t] = dec_fp4_pow2(w[st][t][j], e8m0_decode((sc[st][t] >> ssh) & 0xFFu));
+          for (int t = 0; t < NTW; ++t) {
+            if constexpr (EDW) b[t] = bw[st][t][j];
+            else b[t] = dec_fp4_pow2(w[st][t][j], e8m0_decode((sc[st][t] >> ssh) & 0xFFu));
+          }
 #pragma unroll
           for (int i = 0; i < MT; ++i)
 #pragma unroll
