@@ -180,11 +180,13 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   const int rot = (XLDS && S == 1) ? (int)(blockIdx.x % NW) : 0;  // K-block rotation of the waves
   const int wi = (XLDS && S == 1) ? (wave + rot) % NW : split * NW + wave;
   constexpr bool WFB = XLDS && weights_first<F, WL, MT, NTW>();
-  // early weight decode: weights-first tiles of the 4-bit float formats whose
-  // decoded weights fit beside the activations in registers (16 or 32 rows x
-  // one or two 16-column tiles, two K steps; with two row tiles and two column
-  // tiles it spilled 13-27 registers)
-  constexpr bool EDW = WFB && (F == KF_NVFP4 || F == KF_MXFP4) && SPW * NTW * MT <= 4;
+  // early weight decode: weights-first tiles of the float weight formats
+  // whose decoded weights fit beside the activations in registers (at most
+  // 64 VGPRs of them, and 16 or 32 rows x one or two 16-column tiles: with two
+  // row tiles and two column tiles it spilled 13-27 registers)
+  constexpr int EDJ = (F == KF_FP8) ? 2 : 4;  // decoded 8-element chunks per tile and K step
+  constexpr bool EDW = WFB && (F == KF_NVFP4 || F == KF_MXFP4 || F == KF_FP8) && MT * NTW <= 2 &&
+                       SPW * NTW * EDJ <= 16;
   for (int blk = wi; blk * SPW < T; blk += S * NW) {
     // ---- issue every load of this block before any wait: the activation
     // slices (cache hits; loads return in issue order, so their LDS staging
@@ -229,10 +231,12 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
           // 4-bit weights stream past the caches (non-temporal), which keeps
           // the activations, read by every workgroup, resident: measured at
           // N = 4096, K = 3072, M = 32: INT4 6.7 -> 6.55 us, NVFP4 7.4 -> 7.2,
-          // MXFP4 6.8 -> 6.7; FP8 gained nothing at M = 32 and lost 0.3 us at
-          // M = 1
+          // MXFP4 6.8 -> 6.7.  FP8 gained nothing at M = 32 with 32-row blocks
+          // in the rows layout and lost 0.3 us at M = 1, but gains in tile
+          // order with 16-row blocks (6.20 -> 5.94 us), where it is used
           const uint32_t wo = off_if(kv, w_off<WL>(n, (uint32_t)kbyte<F>(kl), wrow));
-          if constexpr (F == KF_INT4 || F == KF_INT4A || F == KF_NVFP4 || F == KF_MXFP4)
+          if constexpr (F == KF_INT4 || F == KF_INT4A || F == KF_NVFP4 || F == KF_MXFP4 ||
+                        (F == KF_FP8 && WL == kLayoutTiles && MT == 1 && NTW == 2))
             w[st][t] = bload128_nt(Wr, wo);
           else
             w[st][t] = bload128(Wr, wo);
@@ -272,22 +276,24 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     __builtin_amdgcn_sched_barrier(0);
 
     // Early decode (EDW): the weights were issued before the activations and
-    // land first, so the 4-bit float formats decode them while the activation
-    // loads are still in flight.  Same values, same MFMA order.  Measured at
+    // land first, so the float formats decode them while the activation loads
+    // are still in flight.  Same values, same MFMA order.  Measured at
     // N = 4096, K = 3072, M = 32: NVFP4 6.14-6.28 -> 6.07-6.17 us, MXFP4 5.29
-    // -> 5.11 us.
-    bf16x8 bw[EDW ? SPW : 1][EDW ? NTW : 1][EDW ? 4 : 1];
+    // -> 5.11 us, FP8 6.20 -> 6.03 us.
+    bf16x8 bw[EDW ? SPW : 1][EDW ? NTW : 1][EDW ? EDJ : 1];
     if constexpr (EDW) {
 #pragma unroll
       for (int st = 0; st < SPW; ++st)
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < EDJ; ++j) {
             if constexpr (F == KF_NVFP4)
               bw[st][t][j] = dec_fp4_mul(w[st][t][j], e4m3_decode((sc[st][t] >> (ssh + (j < 2 ? 0u : 8u))) & 0xFFu));
-            else
+            else if constexpr (F == KF_MXFP4)
               bw[st][t][j] = dec_fp4_pow2(w[st][t][j], e8m0_decode((sc[st][t] >> ssh) & 0xFFu));
+            else
+              bw[st][t][j] = dec_fp8(w[st][t][2 * j], w[st][t][2 * j + 1]);
           }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -378,7 +384,10 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
         for (int j = 0; j < 2; ++j) {
           bf16x8 b[NTW];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) b[t] = dec_fp8(w[st][t][2 * j], w[st][t][2 * j + 1]);
+          for (int t = 0; t < NTW; ++t) {
+            if constexpr (EDW) b[t] = bw[st][t][j];
+            else b[t] = dec_fp8(w[st][t][2 * j], w[st][t][2 * j + 1]);
+          }
 #pragma unroll
           for (int i = 0; i < MT; ++i)
 #pragma unroll
