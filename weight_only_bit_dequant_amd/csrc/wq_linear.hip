@@ -107,7 +107,9 @@ constexpr bool weights_first() {
   // at N = 4096, K = 3072, M = 32 without -> with: MXFP4 5.42 -> 5.26 us,
   // FP8 6.15 -> 6.06 us, INT4 5.39 -> 5.71 us (INT4_ASYM follows INT4)
   else if constexpr (MT == 1 && NTW == 2) return F == KF_MXFP4 || F == KF_FP8;
-  else return F == KF_MXFP4 || F == KF_NVFP4;
+  // 32-row tiles: MXFP4 and NVFP4 as above; the static FP8 GEMM measured
+  // 5.95 -> 5.63 us (its 16-row blocks, 5.72 us, lost)
+  else return F == KF_MXFP4 || F == KF_NVFP4 || F == KF_FP8S;
 }
 
 // K-split plan of one workgroup: NW waves x SPW macro-steps each per block;
