@@ -136,3 +136,28 @@ def test_mx_large_tiles_with_unaligned_scales():
     ref = MX.forward(X[rows], wc, ws, b)
     assert_close(Y1[torch.as_tensor(rows, device=DEV)], ref, "mx 256 tiles")
     assert_close(Y2[torch.as_tensor(rows, device=DEV)], ref, "mx unaligned scales")
+
+
+@pytest.mark.parametrize("M", [1, 32])
+def test_mx_small_m_dword_scales_same_bits(M):
+    """Up to 64 rows with K % 128 == 0 the kernel loads each step's four block
+    scales as one dword per lane; scale arrays at odd addresses take the byte
+    loads.  Both give the same bits."""
+    N, K = 4096, 3072
+    W, b, X = synth.linear_case(N, K, M, cfg=34 + M)
+    print(f"[case] mx small M, dword vs byte scale loads M={M} N={N} K={K}", flush=True)
+    q = wq.quantize("mxfp4", dev_bf16(W))
+    Xd, bd = dev_bf16(X), dev_bf16(b)
+    Xq, Xs = wq.mx_quantize_act(Xd)
+    Y1 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    wq.wq_mx_linear(Xq, Xs, K, q["packed"], q["scales"], bd, N, Y1)
+    xs_odd = torch.empty(Xs.numel() + 1, dtype=torch.uint8, device=DEV)[1:].view(Xs.shape)
+    xs_odd.copy_(Xs)
+    ws_odd = torch.empty(q["scales"].numel() + 1, dtype=torch.uint8, device=DEV)[1:].view(q["scales"].shape)
+    ws_odd.copy_(q["scales"])
+    Y2 = torch.empty_like(Y1)
+    wq.wq_mx_linear(Xq, xs_odd, K, q["packed"], ws_odd, bd, N, Y2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    wc, ws = Q.quantize_mxfp4(W)
+    assert_close(Y1, MX.forward(X, wc, ws, b), f"mx small M={M}")

@@ -96,7 +96,10 @@ __global__ __launch_bounds__(256) void k_mx_quant_act(const uint16_t* __restrict
 // is issued before the first MFMA; out-of-range offsets read zero codes and
 // zero scale bytes, whose products are zero.  Wave partials are reduced
 // through LDS as in the bf16 kernel.
-template <int MT, int WL>
+// DW (K % 128 == 0): the block scales load as one aligned dword per lane
+// (the step's four E8M0 bytes of the row) and lane group g shifts its byte
+// down; a byte load per lane costs the address unit as much as a 16-byte one.
+template <int MT, int WL, bool DW>
 __global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
   constexpr int NW = 12, SPW = 2, NT = 16;
   constexpr int E = MT * 16 * NT;
@@ -128,18 +131,23 @@ __global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
       const bool kv = k < K;
       const uint32_t n = (uint32_t)(n0 + c);
       w[st] = bload128(Wr, off_if(kv, w_off<WL>(n, (uint32_t)k / 2u, rowb)));
-      ws[st] = bload8(Wsr, off_if(kv, s_off<KF_MXFP4, WL>(n, (uint32_t)k, (uint32_t)K)));
+      const uint32_t wso = s_off<KF_MXFP4, WL>(n, (uint32_t)k, (uint32_t)K);
+      if constexpr (DW) ws[st] = bload32(Wsr, off_if(kv, wso & ~3u));
+      else ws[st] = bload8(Wsr, off_if(kv, wso));
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const uint32_t m = (uint32_t)(m0 + 16 * i + c);
         x[st][i] = bload128(Xr, off_if(kv, m * rowb + (uint32_t)k / 2u));
-        xs[st][i] = bload8(Xsr, off_if(kv, m * srow + (uint32_t)k / 32u));
+        const uint32_t xso = m * srow + (uint32_t)k / 32u;
+        if constexpr (DW) xs[st][i] = bload32(Xsr, off_if(kv, xso & ~3u));
+        else xs[st][i] = bload8(Xsr, off_if(kv, xso));
       }
     }
+    const uint32_t sh = DW ? 8u * (uint32_t)g : 0u;  // byte g of the dword: K block 32g of the step
 #pragma unroll
     for (int st = 0; st < SPW; ++st)
 #pragma unroll
-      for (int i = 0; i < MT; ++i) acc[i] = mfma_mx4(x[st][i], xs[st][i], w[st], ws[st], acc[i]);
+      for (int i = 0; i < MT; ++i) acc[i] = mfma_mx4(x[st][i], xs[st][i] >> sh, w[st], ws[st] >> sh, acc[i]);
   }
 
   // wave partials -> LDS, one barrier, per-thread sums in wave order
@@ -750,10 +758,14 @@ hipError_t launch_mx_linear_l(const LinearArgs& a, hipStream_t s) {
     return t128 >= 192 ? launch_mx_tile<128, 128, WL>(a, s) : launch_mx_tile<64, 64, WL>(a, s);
   }
   const int gx = (a.N + 15) / 16;
+  const bool dw = a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.xscales) & 3) == 0 &&
+                  (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0;
   if (a.M <= 16) {
-    k_mx_linear<1, WL><<<dim3(gx, 1, (a.M + 15) / 16), 768, 0, s>>>(a);
+    if (dw) k_mx_linear<1, WL, true><<<dim3(gx, 1, (a.M + 15) / 16), 768, 0, s>>>(a);
+    else k_mx_linear<1, WL, false><<<dim3(gx, 1, (a.M + 15) / 16), 768, 0, s>>>(a);
   } else {
-    k_mx_linear<2, WL><<<dim3(gx, 1, (a.M + 31) / 32), 768, 0, s>>>(a);
+    if (dw) k_mx_linear<2, WL, true><<<dim3(gx, 1, (a.M + 31) / 32), 768, 0, s>>>(a);
+    else k_mx_linear<2, WL, false><<<dim3(gx, 1, (a.M + 31) / 32), 768, 0, s>>>(a);
   }
   return hipGetLastError();
 }
