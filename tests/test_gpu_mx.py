@@ -161,3 +161,40 @@ def test_mx_small_m_dword_scales_same_bits(M):
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
     wc, ws = Q.quantize_mxfp4(W)
     assert_close(Y1, MX.forward(X, wc, ws, b), f"mx small M={M}")
+
+
+@pytest.mark.parametrize("M,N,K,bias", [
+    # the mid-M kernel: more than 64 rows up to 256 tiles of 64 x 64,
+    # K % 512 == 0, 1024 <= K <= 4096
+    (65, 4096, 1024, True),    # first row count above the small-M kernel; one block per wave, last row tile holds one row
+    (200, 1056, 1536, True),   # ragged M and N tiles (N % 64 = 32); 12 blocks: waves 0-3 take two
+    (256, 4096, 3072, False),  # 3 blocks per wave, no bias
+    (256, 4096, 2560, True),   # 20 blocks: 3 or 2 per wave
+    (129, 512, 4096, True),    # the longest K: 4 blocks per wave, 128 KiB of activation rows in LDS
+    (1024, 1024, 2048, True),  # 256 tiles; sampled rows
+    # the same range outside its limits: the 64 x 64 tiled kernel
+    (200, 1056, 1152, True),   # K % 512 != 0
+    (130, 256, 9216, True),    # K > 4096
+    (768, 4096, 1024, True),   # 768 tiles; sampled rows
+])
+def test_mx_mid_kernel(M, N, K, bias):
+    """The mid-M MX kernel (8 waves split K; activation rows and block scales
+    loaded whole into LDS) and, past its limits, the tiled kernel: both weight
+    layouts give the same bits, and a repeated call too (fixed-order
+    reduction)."""
+    W, b, X = synth.linear_case(N, K, M, cfg=600 + M % 50)
+    b = b if bias else None
+    print(f"[case] mx mid M={M} N={N} K={K} bias={bias}", flush=True)
+    q = wq.quantize("mxfp4", dev_bf16(W))
+    qt = wq.repack(q, wq.LAYOUT_TILES)
+    Xd, bd = dev_bf16(X), dev_bf16(b) if b is not None else None
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wq.mxfp4_dynamic_linear(Xd, q, bd, out=Y)
+    Yt = wq.mxfp4_dynamic_linear(Xd, qt, bd)
+    Y2 = wq.mxfp4_dynamic_linear(Xd, q, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yt.view(torch.int16)), "layouts differ"
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), "repeated call differs"
+    wc, ws = Q.quantize_mxfp4(W)
+    rows = np.arange(M) if M <= 512 else np.arange(0, M, 29)
+    assert_close(Y[torch.as_tensor(rows, device=DEV)], MX.forward(X[rows], wc, ws, b), f"mx mid M={M} N={N} K={K}")

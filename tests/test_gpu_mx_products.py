@@ -1,13 +1,14 @@
 """The scaled E2M1 x E2M1 matrix-core path (MXFP4 page: MX activations x MX
 weights) against the closed forms of E2M1 and E8M0, product by product.
 
-Activation row m carries code m % 16 at one K position (7m % 128) under block
+Activation row m carries code m % 16 at one K position (7m % K) under block
 scale 2^((m / 16) % 16 - 7), zeros elsewhere; weight row n carries code n % 16
 at every K position under block scale 2^((n / 16) % 16 - 7).  Without bias,
 Y[m][n] is the single product of the two scaled values: at most 4 significant
 bits and within bf16's normal range, so the bf16 output must equal it exactly
 (a zero product is +0, as the accumulation starts from +0).  The shapes reach
-the small-M kernel, the tiled kernel and the 256 x 256 kernel."""
+the small-M kernel, the tiled kernel, the mid-M kernel (K = 1024) and the
+256 x 256 kernel."""
 
 import numpy as np
 import pytest
@@ -20,7 +21,6 @@ wq = pytest.importorskip("weight_only_bit_dequant_amd.wq")
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-K = 128
 
 
 def _pack(codes):
@@ -28,8 +28,8 @@ def _pack(codes):
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
 
 
-@pytest.mark.parametrize("M,N", [(64, 256), (256, 256), (4096, 3072)])
-def test_e2m1_products_exact(M, N):
+@pytest.mark.parametrize("M,N,K", [(64, 256, 128), (256, 256, 128), (256, 256, 1024), (4096, 3072, 128)])
+def test_e2m1_products_exact(M, N, K):
     m, n = np.arange(M), np.arange(N)
     a, b = (m % 16).astype(np.uint8), (n % 16).astype(np.uint8)
     sa, sb = (120 + (m // 16) % 16).astype(np.uint8), (120 + (n // 16) % 16).astype(np.uint8)
@@ -43,7 +43,7 @@ def test_e2m1_products_exact(M, N):
     ref = np.outer(va, vb) + 0.0
     ref_bits = C.f64_to_bf16(ref)
     assert np.array_equal(C.bf16_to_f32(ref_bits).astype(np.float64), ref), "products are exact in bf16"
-    print(f"[case] e2m1 products M={M} N={N}", flush=True)
+    print(f"[case] e2m1 products M={M} N={N} K={K}", flush=True)
     Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     wq.wq_mx_linear(dev(_pack(Xc)), dev(Xs), K, dev(_pack(Wc)), dev(Ws), None, N, Y)

@@ -165,6 +165,196 @@ __global__ __launch_bounds__(768) void k_mx_linear(LinearArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- mid-M GEMM
+// One workgroup of 8 waves owns a 64 x 64 output tile and its waves split K:
+// wave w takes the 128-K blocks w, w + 8, ... and accumulates all 16 of the
+// tile's 16 x 16 outputs for them, so the waves meet only twice: once when
+// the activations are in LDS and once for the reduction at the end.
+//  * The workgroup's 64 packed activation rows (all of K) and the block scales
+//    of its rows and columns go from memory straight into LDS (buffer_load
+//    ... lds), 64 lanes x 16 bytes per instruction: every instruction reads
+//    whole 128-byte lines.  Loaded in the MFMA operand layout instead, each
+//    instruction would touch 16 rows for 64 bytes each, and each scale dword
+//    load 16 lines for 4 bytes each; those requests, not the bytes, bound
+//    that form (10.6 us at M = 256, N = 4096, K = 3072, the same as the
+//    64 x 64 LDS-tiled kernel; 8.0 us without the scale loads, 7.8 us without
+//    the activation loads, 10.6 us without the MFMAs).
+//  * The packed weights of the wave's blocks are loaded into registers up
+//    front: lane (g, c) takes the 16 bytes of column c at K 32g .. 32g+31 of
+//    the block (in tile order one instruction reads one whole 1 KiB tile).
+//  * Activation rows in LDS keep the memory order of their 16-byte chunks
+//    except for an XOR of chunk bits 1-3 with row bits 0-2: the operand reads
+//    of rows c = 0..7 by lane groups g and g + 1 (one ds_read_b128 cycle) then
+//    hit 16 distinct bank groups.  Needs K % 512 == 0 (16-chunk row groups).
+// Rows past M, columns past N read zeros.  K % 512 == 0, K <= kMxMidMaxK,
+// 4-byte aligned scale arrays.
+constexpr int kMxMidWaves = 8, kMxMidT = 64, kMxMidPW = kMxMidT + 4;
+constexpr int kMxMidMaxK = 4096;
+constexpr int kMxMidNB = kMxMidMaxK / 128 / kMxMidWaves;  // blocks per wave at most
+constexpr int kMxMidXBytes = kMxMidT * kMxMidMaxK / 2;     // activation rows
+constexpr int kMxMidSBytes = kMxMidT * kMxMidMaxK / 32;    // one scale plane
+constexpr int kMxMidPart = kMxMidWaves * kMxMidT * kMxMidPW * 4;
+constexpr int kMxMidSmem = (kMxMidXBytes + 2 * kMxMidSBytes) > kMxMidPart ? (kMxMidXBytes + 2 * kMxMidSBytes) : kMxMidPart;
+
+__device__ __forceinline__ uint32_t mx_mid_swz(uint32_t row, uint32_t chunk) { return chunk ^ ((row & 7u) << 1); }
+
+// copy `bytes` (a multiple of 16) from r at `src` to LDS at `dst`, 16 bytes
+// per lane, the workgroup's 512 lanes in turn; chunks past the resource read zero
+__device__ __forceinline__ void mx_mid_copy(unsigned char* dst, __amdgpu_buffer_rsrc_t r, uint32_t src, uint32_t bytes,
+                                            int wave, int lane) {
+  for (uint32_t p = (uint32_t)wave * 64u; p < bytes / 16u; p += kMxMidWaves * 64u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + p * 16u), 16,
+                                             src + (p + (uint32_t)lane) * 16u, 0, 0, 0);
+}
+
+template <int WL, int NB>
+__global__ __launch_bounds__(kMxMidWaves * 64) void k_mx_mid(LinearArgs a) {
+  constexpr int T = kMxMidT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int M = a.M, N = a.N, K = a.K;
+  const int n0 = blockIdx.x * T, m0 = blockIdx.y * T;
+  const int KT = K / 128;
+  const uint32_t rowb = (uint32_t)K / 2u, srow = (uint32_t)K / 32u, C = rowb / 16u;  // C: chunks per row
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * rowb);
+  const __amdgpu_buffer_rsrc_t Wsr = make_rsrc(a.scales, (uint32_t)N * srow);
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * rowb);
+  const __amdgpu_buffer_rsrc_t Xsr = make_rsrc(a.xscales, (uint32_t)M * srow);
+  unsigned char* xl = smem;                       // [64][K/2] activation rows, swizzled chunks
+  unsigned char* xsl = smem + 64 * rowb;          // [64][K/32] activation block scales
+  unsigned char* wsl = xsl + 64 * srow;           // the weight block scales of the 64 columns
+
+  // weights of this wave's blocks into registers
+  u32x4 w[NB][4];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int kb = wave + j * kMxMidWaves;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      w[j][t] = bload128(Wr, off_if(kb < KT, w_off<WL>((uint32_t)(n0 + 16 * t + c), (uint32_t)(kb * 64 + 16 * g), rowb)));
+  }
+  // activation rows: LDS chunk p = row * C + k holds memory chunk k ^ swz of that row
+  {
+    const uint32_t step = kMxMidWaves * 64u, dq = step / C, dr = step % C;  // C is a multiple of 16, <= 128
+    uint32_t p = (uint32_t)wave * 64u + (uint32_t)lane;
+    uint32_t row = p / C, k = p % C;
+    for (uint32_t p0 = (uint32_t)wave * 64u; p0 < 64u * C; p0 += step) {
+      const uint32_t src = (((uint32_t)m0 + row) * C + mx_mid_swz(row, k)) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (__attribute__((address_space(3))) void*)(xl + p0 * 16u), 16, src, 0, 0, 0);
+      row += dq;
+      k += dr;
+      if (k >= C) {
+        k -= C;
+        ++row;
+      }
+    }
+  }
+  // block scales: the 64 activation rows are contiguous, and so are the 64
+  // columns' weight scales in either layout
+  mx_mid_copy(xsl, Xsr, (uint32_t)m0 * srow, 64u * srow, wave, lane);
+  mx_mid_copy(wsl, Wsr, WL == kLayoutTiles ? (uint32_t)(n0 / 16) * (uint32_t)KT * 64u : (uint32_t)n0 * srow, 64u * srow, wave,
+              lane);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads, LDS ones included
+  __syncthreads();
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t sh = 8u * (uint32_t)g;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int kb = wave + j * kMxMidWaves;
+    if (kb >= KT) break;  // wave-uniform
+    u32x4 x[4];
+    uint32_t xs[4], ws[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t row = (uint32_t)(16 * i + c);
+      x[i] = *reinterpret_cast<const u32x4*>(xl + (row * C + mx_mid_swz(row, (uint32_t)(4 * kb + g))) * 16u);
+      xs[i] = *reinterpret_cast<const uint32_t*>(xsl + row * srow + 4u * (uint32_t)kb);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t so = WL == kLayoutTiles ? (((uint32_t)t * (uint32_t)KT + (uint32_t)kb) * 16u + (uint32_t)c) * 4u
+                                             : (uint32_t)(16 * t + c) * srow + 4u * (uint32_t)kb;
+      ws[t] = *reinterpret_cast<const uint32_t*>(wsl + so);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[i][t] = mfma_mx4(x[i], xs[i] >> sh, w[j][t], ws[t] >> sh, acc[i][t]);
+  }
+  __syncthreads();  // every wave is done with the operands in LDS
+
+  // partials of wave w: rows w * 64 .. w * 64 + 63 (stride kMxMidPW floats)
+  float* part = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[(wave * T + 16 * i + 4 * g + r) * kMxMidPW + 16 * t + c] = acc[i][t][r];
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  // one item per thread: 8 consecutive outputs of one row, wave partials summed in wave order
+  static_assert(T * (T / 8) == kMxMidWaves * 64, "one output item per thread");
+  const int row = tid / (T / 8), cg = tid % (T / 8);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+#pragma unroll
+  for (int w2 = 0; w2 < kMxMidWaves; ++w2) {
+    const float* pp = part + (w2 * T + row) * kMxMidPW + 8 * cg;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(pp), hi = *reinterpret_cast<const f32x4*>(pp + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] += lo[e];
+      v[4 + e] += hi[e];
+    }
+  }
+  const int m = m0 + row, nn = n0 + 8 * cg;
+  const u32x4 bb = bload128(Br, (uint32_t)nn * 2u);  // zero past N and without bias
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float b0 = bitsf(bb[q] << 16), b1 = bitsf(bb[q] & 0xFFFF0000u);
+    o[q] = (uint32_t)f32_to_bf16(v[2 * q] + b0) | ((uint32_t)f32_to_bf16(v[2 * q + 1] + b1) << 16);
+  }
+  if (m < M) {
+    if (nn + 8 <= N && (N & 7) == 0) {
+      __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4*>(a.Y + (int64_t)m * N + nn));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (nn + e < N) a.Y[(int64_t)m * N + nn + e] = (uint16_t)(o[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+template <int WL, int NB>
+hipError_t launch_mx_mid_nb(const LinearArgs& a, hipStream_t s) {
+  static_assert(kMxMidSmem <= 160 * 1024, "exceeds the LDS of a CU");
+  static std::atomic<int> done{0};
+  auto k = k_mx_mid<WL, NB>;
+  hipError_t e = allow_smem(k, kMxMidSmem, done);
+  if (e != hipSuccess) return e;
+  k<<<dim3((a.N + kMxMidT - 1) / kMxMidT, (a.M + kMxMidT - 1) / kMxMidT), kMxMidWaves * 64, kMxMidSmem, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int WL>
+hipError_t launch_mx_mid(const LinearArgs& a, hipStream_t s) {
+  const int nb = (a.K / 128 + kMxMidWaves - 1) / kMxMidWaves;
+  if (nb <= 2) return launch_mx_mid_nb<WL, 2>(a, s);
+  if (nb <= 3) return launch_mx_mid_nb<WL, 3>(a, s);
+  return launch_mx_mid_nb<WL, kMxMidNB>(a, s);
+}
+
 // ---------------------------------------------------------------- tiled GEMM (larger M)
 // One workgroup (4 waves, 2 x 2) computes a BM x BN tile; K advances 128 per
 // step (one scaled MFMA deep).  Per step every thread loads its share of the
@@ -742,9 +932,9 @@ hipError_t launch_f8_gemm_tiled_l(const LinearArgs& a, hipStream_t s) {
 template <int WL>
 hipError_t launch_mx_linear_l(const LinearArgs& a, hipStream_t s) {
   if (a.M > 64) {
-    // matrix-core bound: 256 x 256 tiles straight into LDS when they fill the
-    // chip (whole scale dwords per row needed), else 128 x 128 or 64 x 64
-    // through registers
+    // 256 x 256 tiles straight into LDS when they fill the chip (whole scale
+    // dwords per row needed); up to one round of 64 x 64 tiles the mid-M
+    // kernel; else 128 x 128 or 64 x 64 through registers
     const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (t256 >= 192 && a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.xscales) & 3) == 0 &&
         (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0) {
@@ -754,6 +944,10 @@ hipError_t launch_mx_linear_l(const LinearArgs& a, hipStream_t s) {
       k_mx_gemm256<WL><<<dim3((a.N + kMxT - 1) / kMxT, (a.M + kMxT - 1) / kMxT), 1024, kMxSmem, s>>>(a);
       return hipGetLastError();
     }
+    const int64_t t64 = (int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64);
+    if (t64 <= 256 && a.K % 512 == 0 && a.K >= 1024 && a.K <= kMxMidMaxK && (reinterpret_cast<uintptr_t>(a.xscales) & 3) == 0 &&
+        (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0)
+      return launch_mx_mid<WL>(a, s);
     const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
     return t128 >= 192 ? launch_mx_tile<128, 128, WL>(a, s) : launch_mx_tile<64, 64, WL>(a, s);
   }
