@@ -140,9 +140,10 @@ def test_mx_large_tiles_with_unaligned_scales():
 
 @pytest.mark.parametrize("M", [1, 32])
 def test_mx_small_m_dword_scales_same_bits(M):
-    """Up to 64 rows with K % 128 == 0 the kernel loads each step's four block
-    scales as one dword per lane; scale arrays at odd addresses take the byte
-    loads.  Both give the same bits."""
+    """Up to 64 rows with K % 128 == 0 the block scales load as dwords (from 9
+    rows with K % 512 == 0 the activation rows and scale rows through LDS);
+    scale arrays at odd addresses take byte loads straight into registers.
+    Both give the same bits."""
     N, K = 4096, 3072
     W, b, X = synth.linear_case(N, K, M, cfg=34 + M)
     print(f"[case] mx small M, dword vs byte scale loads M={M} N={N} K={K}", flush=True)
@@ -198,3 +199,31 @@ def test_mx_mid_kernel(M, N, K, bias):
     wc, ws = Q.quantize_mxfp4(W)
     rows = np.arange(M) if M <= 512 else np.arange(0, M, 29)
     assert_close(Y[torch.as_tensor(rows, device=DEV)], MX.forward(X[rows], wc, ws, b), f"mx mid M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (24, 1024, 4096),   # activations through LDS: two passes of 24 steps (4 steps per wave)
+    (40, 512, 8192),    # the longest K through LDS: 6 steps per wave, two row blocks
+    (16, 256, 512),     # 4 steps: waves 2-11 have none
+    (9, 4096, 3072),    # the first row count through LDS
+    (8, 4096, 640),     # K % 512 != 0: operands straight into registers, dword scales
+    (64, 256, 1152),    # the same with two row tiles per block
+    (48, 256, 16384),   # K past the LDS limit: straight into registers
+])
+def test_mx_small_m_kernels(M, N, K):
+    """9 to 64 rows: with K % 512 == 0 and K <= 8192 the workgroup copies its
+    activation rows and scale rows into LDS; otherwise (and up to 8 rows) the
+    operands load straight into registers.  Both weight layouts give the same
+    bits."""
+    W, b, X = synth.linear_case(N, K, M, cfg=650 + M)
+    print(f"[case] mx small M={M} N={N} K={K}", flush=True)
+    q = wq.quantize("mxfp4", dev_bf16(W))
+    qt = wq.repack(q, wq.LAYOUT_TILES)
+    Xd, bd = dev_bf16(X), dev_bf16(b)
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wq.mxfp4_dynamic_linear(Xd, q, bd, out=Y)
+    Yt = wq.mxfp4_dynamic_linear(Xd, qt, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yt.view(torch.int16)), "layouts differ"
+    wc, ws = Q.quantize_mxfp4(W)
+    assert_close(Y, MX.forward(X, wc, ws, b), f"mx small M={M} N={N} K={K}")

@@ -7,8 +7,8 @@ at every K position under block scale 2^((n / 16) % 16 - 7).  Without bias,
 Y[m][n] is the single product of the two scaled values: at most 4 significant
 bits and within bf16's normal range, so the bf16 output must equal it exactly
 (a zero product is +0, as the accumulation starts from +0).  The shapes reach
-the small-M kernel, the tiled kernel, the mid-M kernel (K = 1024) and the
-256 x 256 kernel."""
+the two small-M kernels (K = 128 and 512), the tiled kernel, the mid-M
+kernel (K = 1024) and the 256 x 256 kernel."""
 
 import numpy as np
 import pytest
@@ -28,7 +28,7 @@ def _pack(codes):
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 256, 128), (256, 256, 128), (256, 256, 1024), (4096, 3072, 128)])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 128), (64, 256, 512), (256, 256, 128), (256, 256, 1024), (4096, 3072, 128)])
 def test_e2m1_products_exact(M, N, K):
     m, n = np.arange(M), np.arange(N)
     a, b = (m % 16).astype(np.uint8), (n % 16).astype(np.uint8)

@@ -355,6 +355,137 @@ hipError_t launch_mx_mid(const LinearArgs& a, hipStream_t s) {
   return launch_mx_mid_nb<WL, kMxMidNB>(a, s);
 }
 
+// ---------------------------------------------------------------- small-M GEMM, activations through LDS
+// k_mx_linear's workgroup (12 waves, 16 columns x 16*MT rows x all of K, wave
+// w taking the 128-K steps 2w, 2w + 1, 2w + 24, ...) with its activations
+// copied into LDS first: the 16*MT packed rows (all of K) and their block
+// scale rows go from memory straight into LDS as whole 128-byte lines
+// (buffer_load ... lds, chunks swizzled as in the mid-M kernel), instead of
+// 16 rows x 64 bytes and 16 rows x 4 bytes per instruction.  Each wave loads
+// its steps' packed weights and weight scale dwords into registers up front,
+// waits at one barrier and runs its MFMAs from LDS and registers.  NS: steps
+// per wave at most (2 per 24-step pass).  K % 512 == 0, K <= kMxSmallMaxK.
+constexpr int kMxSmallMaxK = 8192;
+
+template <int MT, int WL, int NS>
+__global__ __launch_bounds__(768) void k_mx_small(LinearArgs a) {
+  constexpr int NW = 12, NT = 16, R = 16 * MT;
+  constexpr int E = MT * 16 * NT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int n0 = blockIdx.x * NT, m0 = blockIdx.z * R;
+  const int M = a.M, N = a.N, K = a.K;
+  const int T = K / 128;
+  const uint32_t rowb = (uint32_t)K / 2u, srow = (uint32_t)K / 32u, C = rowb / 16u;
+  const __amdgpu_buffer_rsrc_t Wr = make_rsrc(a.W, (uint32_t)N * rowb);
+  const __amdgpu_buffer_rsrc_t Wsr = make_rsrc(a.scales, (uint32_t)N * srow);
+  const __amdgpu_buffer_rsrc_t Xr = make_rsrc(a.X, (uint32_t)M * rowb);
+  const __amdgpu_buffer_rsrc_t Xsr = make_rsrc(a.xscales, (uint32_t)M * srow);
+  const __amdgpu_buffer_rsrc_t Br = make_rsrc(a.bias ? (const void*)a.bias : a.W, a.bias ? (uint32_t)N * 2u : 0u);
+  const int en = n0 + tid % NT;
+  const uint32_t bias_bits = bload16(Br, (uint32_t)en * 2u);
+  unsigned char* xl = smem;                       // [R][K/2] activation rows, swizzled chunks
+  unsigned char* xsl = smem + R * rowb;           // [R][K/32] activation block scales
+  auto step_of = [&](int j) { return 2 * wave + (j & 1) + (j >> 1) * (2 * NW); };
+
+  // this wave's packed weights and weight scale dwords
+  const uint32_t n = (uint32_t)(n0 + c);
+  u32x4 w[NS];
+  uint32_t ws[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int st = step_of(j);
+    const bool ok = st < T;
+    w[j] = bload128(Wr, off_if(ok, w_off<WL>(n, (uint32_t)(st * 64 + 16 * g), rowb)));
+    ws[j] = bload32(Wsr, off_if(ok, s_off<KF_MXFP4, WL>(n, (uint32_t)(st * 128), (uint32_t)K)));
+  }
+  // activation rows: LDS chunk p = row * C + k holds memory chunk k ^ swz of that row
+  {
+    const uint32_t step = NW * 64u, dq = step / C, dr = step % C;
+    uint32_t p = (uint32_t)wave * 64u + (uint32_t)lane;
+    uint32_t row = p / C, k = p % C;
+    for (uint32_t p0 = (uint32_t)wave * 64u; p0 < (uint32_t)R * C; p0 += step) {
+      const uint32_t src = (((uint32_t)m0 + row) * C + mx_mid_swz(row, k)) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Xr, (__attribute__((address_space(3))) void*)(xl + p0 * 16u), 16, src, 0, 0, 0);
+      row += dq;
+      k += dr;
+      if (k >= C) {
+        k -= C;
+        ++row;
+      }
+    }
+  }
+  // the rows' block scales (contiguous); the LDS region is rounded up to whole
+  // 1 KiB instructions
+  for (uint32_t p0 = (uint32_t)wave * 64u; p0 * 16u < (uint32_t)R * srow; p0 += NW * 64u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(Xsr, (__attribute__((address_space(3))) void*)(xsl + p0 * 16u), 16,
+                                             (uint32_t)m0 * srow + (p0 + (uint32_t)lane) * 16u, 0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads, LDS ones included
+  __syncthreads();
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t sh = 8u * (uint32_t)g;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int st = step_of(j);
+    if (st >= T) break;  // wave-uniform; steps grow with j
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const uint32_t row = (uint32_t)(16 * i + c);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(xl + (row * C + mx_mid_swz(row, (uint32_t)(4 * st + g))) * 16u);
+      const uint32_t xs = *reinterpret_cast<const uint32_t*>(xsl + row * srow + 4u * (uint32_t)st);
+      acc[i] = mfma_mx4(x, xs >> sh, w[j], ws[j] >> sh, acc[i]);
+    }
+  }
+  __syncthreads();  // the partials reuse the activation rows' LDS
+
+  // wave partials -> LDS, one barrier, per-thread sums in wave order
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) *reinterpret_cast<f32x4*>(red + ((wave * MT + i) * 64 + lane) * 4) = acc[i];
+  __syncthreads();
+  if (tid < E) {
+    const int row = tid / NT, col = tid % NT;
+    const int idx = ((row >> 4) * 64 + 16 * ((row >> 2) & 3) + col) * 4 + (row & 3);
+    float v = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) v += red[w2 * E + idx];
+    const int m = m0 + row;
+    if (m < M && en < N) a.Y[(int64_t)m * N + en] = f32_to_bf16(v + bitsf(bias_bits << 16));
+  }
+}
+
+// LDS bytes of k_mx_small: activation rows plus scale rows (rounded up to
+// 1 KiB), or the wave partials if larger
+__host__ __device__ constexpr int mx_small_smem(int MT, int K) {
+  const int rows = 16 * MT * K / 2 + (16 * MT * K / 32 + 1023) / 1024 * 1024;
+  const int red = 12 * MT * 16 * 16 * 4;
+  return rows > red ? rows : red;
+}
+
+template <int MT, int WL, int NS>
+hipError_t launch_mx_small_ns(const LinearArgs& a, hipStream_t s) {
+  static_assert(mx_small_smem(MT, kMxSmallMaxK) <= 160 * 1024, "exceeds the LDS of a CU");
+  static std::atomic<int> done{0};
+  auto k = k_mx_small<MT, WL, NS>;
+  hipError_t e = allow_smem(k, mx_small_smem(MT, kMxSmallMaxK), done);
+  if (e != hipSuccess) return e;
+  k<<<dim3((a.N + 15) / 16, 1, (a.M + 16 * MT - 1) / (16 * MT)), 768, mx_small_smem(MT, a.K), s>>>(a);
+  return hipGetLastError();
+}
+
+template <int MT, int WL>
+hipError_t launch_mx_small(const LinearArgs& a, hipStream_t s) {
+  const int passes = (a.K / 128 + 23) / 24;
+  if (passes <= 1) return launch_mx_small_ns<MT, WL, 2>(a, s);
+  if (passes <= 2) return launch_mx_small_ns<MT, WL, 4>(a, s);
+  return launch_mx_small_ns<MT, WL, 6>(a, s);  // K <= 8192: 64 steps
+}
+
 // ---------------------------------------------------------------- tiled GEMM (larger M)
 // One workgroup (4 waves, 2 x 2) computes a BM x BN tile; K advances 128 per
 // step (one scaled MFMA deep).  Per step every thread loads its share of the
@@ -954,6 +1085,11 @@ hipError_t launch_mx_linear_l(const LinearArgs& a, hipStream_t s) {
   const int gx = (a.N + 15) / 16;
   const bool dw = a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.xscales) & 3) == 0 &&
                   (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0;
+  // activations through LDS from 9 rows on (M = 1 / 8 / 12 / 32 at N = 4096,
+  // K = 3072: 3.48 / 3.74 / 4.01 / 5.81 us straight into registers against
+  // 3.65 / 3.75 / 3.82 / 4.42 us through LDS)
+  if (dw && a.M > 8 && a.K % 512 == 0 && a.K <= kMxSmallMaxK)
+    return a.M <= 16 ? launch_mx_small<1, WL>(a, s) : launch_mx_small<2, WL>(a, s);
   if (a.M <= 16) {
     if (dw) k_mx_linear<1, WL, true><<<dim3(gx, 1, (a.M + 15) / 16), 768, 0, s>>>(a);
     else k_mx_linear<1, WL, false><<<dim3(gx, 1, (a.M + 15) / 16), 768, 0, s>>>(a);
