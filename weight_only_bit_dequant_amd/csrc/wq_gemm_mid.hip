@@ -47,9 +47,6 @@ constexpr int kMidMT = kMidBM / 16, kMidNT = kMidBN / 16;
 constexpr int kMidSlot = kMidBM * 256;  // one 128-K block of 64 activation rows
 constexpr int kMidPW = kMidBN + 4;      // partial row stride (floats)
 
-// s_waitcnt immediates: vmcnt(0) (other counters untouched), lgkmcnt(0)
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitLgkm0 = 0xC07F;
 
 // LDS position of 16-byte chunk k of activation row r (16 chunks per row): the
 // reads of lane groups g (chunk 4g + kk) of 16 rows hit 16 distinct 16-byte

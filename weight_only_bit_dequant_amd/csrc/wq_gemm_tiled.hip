@@ -500,7 +500,7 @@ __global__ __launch_bounds__(NW * 64) void k_woq_gemm256(LinearArgs a) {
       // this wave's loads are done: activations of step kt+h in LDS, weight
       // registers of step kt+h+1; after the barrier every wave's are, and
       // stage (kt+h+1)&1 is no longer read
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       issueX(kt + h + 1, (h + 1) & 1);
       loadW(kt + h + 2, wb[h], sb[h]);
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(NW * 64) void k_woq_gemm256(LinearArgs a) {
     }
   }
   // no LDS write may still be in flight when the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   float s1 = 1.0f;
   if constexpr (F == KF_NVFP4) s1 = a.gscale[0];
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(512) void k_mx_wreg(LinearArgs a) {
     for (int h = 0; h < 2; ++h) {
       // this wave's loads of step kt+h are done; after the barrier every
       // wave's are, and stage (kt+h+1)&1 is no longer read
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       issueX(kt + h + 1, (h + 1) & 1);
       loadW(kt + h + 1, wr[(h + 1) & 1]);
@@ -667,7 +667,7 @@ __global__ __launch_bounds__(512) void k_mx_wreg(LinearArgs a) {
     }
   }
   // no LDS write may still be in flight when the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // epilogue through LDS
   __syncthreads();  // every wave is done with the activation stages

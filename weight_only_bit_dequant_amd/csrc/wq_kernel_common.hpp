@@ -185,6 +185,12 @@ __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 constexpr uint32_t kOOB = 0x80000000u;  // beyond every resource (sizes are < 2^31)
 
+// s_waitcnt immediates (gfx9 encoding): vmcnt(0) with the other counters left
+// alone, and lgkmcnt(0) likewise.  Loads into LDS (buffer_load ... lds) count
+// in vmcnt, so vmcnt(0) also means this wave's LDS copies have landed.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
 // `off` when `ok`, else an offset past every resource -- computed with bit
 // operations so the compiler cannot split the load into guarded branches
 // (each branch join would drain the loads in flight).

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kMxMidWaves * 64) void k_mx_mid(LinearArgs a) {
   mx_mid_copy(xsl, Xsr, (uint32_t)m0 * srow, 64u * srow, wave, lane);
   mx_mid_copy(wsl, Wsr, WL == kLayoutTiles ? (uint32_t)(n0 / 16) * (uint32_t)KT * 64u : (uint32_t)n0 * srow, 64u * srow, wave,
               lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads, LDS ones included
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads, LDS ones included
   __syncthreads();
 
   f32x4 acc[4][4];
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(768) void k_mx_small(LinearArgs a) {
   for (uint32_t p0 = (uint32_t)wave * 64u; p0 * 16u < (uint32_t)R * srow; p0 += NW * 64u)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(Xsr, (__attribute__((address_space(3))) void*)(xsl + p0 * 16u), 16,
                                              (uint32_t)m0 * srow + (p0 + (uint32_t)lane) * 16u, 0, 0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads, LDS ones included
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads, LDS ones included
   __syncthreads();
 
   f32x4 acc[MT];
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(kF8Waves * 64) void k_f8_gemm256(LinearArgs a) {
     colv[kF8T + tid] = bitsf(bload16(Br, (uint32_t)(n0 + tid) * 2u) << 16);
   }
   for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of step kt are in LDS
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of step kt are in LDS
     __syncthreads();                     // ... and every wave's; stage (kt+1)&1 is no longer read
     if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
     const unsigned char* A = smem + (kt & 1) * kF8Stage;
@@ -959,7 +959,7 @@ __global__ __launch_bounds__(1024) void k_mx_gemm256(LinearArgs a) {
   float* colb = reinterpret_cast<float*>(smem + kMxColb);
   if (tid < kMxT) colb[tid] = bitsf(bload16(Br, (uint32_t)(n0 + tid) * 2u) << 16);
   for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of step kt are in LDS
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of step kt are in LDS
     __syncthreads();                     // ... and every wave's; stage (kt+1)&1 is no longer read
     if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
     const unsigned char* base = smem + (kt & 1) * kMxStage;
