@@ -4,7 +4,8 @@ the MXFP4 dynamic-activation Linear (MX act Q + scaled FP4 GEMM).  The
 regimes put every launch configuration of their GEMMs under ragged M, N and
 K: one/two rows, the 16- and 32-row small-M kernels (with two row blocks),
 the split-K path of narrow layers, and the tiled kernels (64 x 64, 128 x 128
-and, for the large shapes, 256 x 256 tiles).  Outputs are compared with the
+and, for the large shapes, 256 x 256 tiles); two more MX regimes with
+K % 512 == 0 reach the GEMMs that copy the activations into LDS.  Outputs are compared with the
 oracle's fp64 result at the parity bar (relative Frobenius error 1e-2) on
 every row up to 512 rows, else on a sample of rows.  WQ_SWEEP_SEED and
 WQ_SWEEP_PER_REGIME draw another or a larger sweep."""
@@ -45,6 +46,21 @@ for _i, (_mr, _nr, _kr) in enumerate(REGIMES):
         for _path in ("static", "mx"):
             CASES.append((_path, int(_rng.randint(_mr[0], _mr[1] + 1)), int(_rng.randint(_nr[0], _nr[1] + 1)),
                           int(_rng.randint(_kr[0], _kr[1] + 1)), 800 + 2 * (_PER * _i + _j) + (_path == "mx")))
+
+
+# MX regimes with K % 512 == 0, where the MX GEMMs copy the packed activation
+# rows and block scales into LDS: the small-M kernel (9 to 64 rows, K up to
+# 8192) and the mid-M kernel (65 to 512 rows, N <= 2048: at most 256 tiles of
+# 64 x 64, 1024 <= K <= 4096)
+MX512_REGIMES = [
+    ((9, 64), (512, 4160), (1, 16)),
+    ((65, 512), (256, 2048), (2, 8)),
+]
+MX512_CASES = []
+for _i, (_mr, _nr, _kr) in enumerate(MX512_REGIMES):
+    for _j in range(_PER):
+        MX512_CASES.append((int(_rng.randint(_mr[0], _mr[1] + 1)), int(_rng.randint(_nr[0], _nr[1] + 1)),
+                            512 * int(_rng.randint(_kr[0], _kr[1] + 1)), 900 + _PER * _i + _j))
 
 
 def dev_bf16(bits):
@@ -92,3 +108,17 @@ def test_act_quant_linear_sweep(path, M, N, K, cfg):
         wc, ws = Q.quantize_mxfp4(W)
         ref = MX.forward(X[rows], wc, ws, b)
     assert_close(Y[torch.as_tensor(rows, device=DEV)], ref, f"{path} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K,cfg", MX512_CASES)
+def test_mx_lds_kernels_sweep(M, N, K, cfg):
+    N = max(32, N // 32 * 32)
+    W, b, X = synth.linear_case(N, K, M, cfg=cfg, bias=(cfg % 2 == 0))
+    print(f"[case] mx K%512 sweep M={M} N={N} K={K} bias={b is not None}", flush=True)
+    bd = dev_bf16(b) if b is not None else None
+    q = wq.quantize("mxfp4", dev_bf16(W))
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wq.mxfp4_dynamic_linear(dev_bf16(X), q, bd, out=Y)
+    torch.cuda.synchronize()
+    wc, ws = Q.quantize_mxfp4(W)
+    assert_close(Y, MX.forward(X, wc, ws, b), f"mx M={M} N={N} K={K}")
