@@ -17,8 +17,9 @@
 //    wait, as buffer loads whose out-of-range offsets read
 //    zero (no branches around loads);
 //  * activations (M <= 32 rows per workgroup) are loaded with contiguous
-//    16-byte loads into a private LDS slot per wave and read back in the
-//    MFMA operand layout;
+//    16-byte loads into a private LDS slot per wave (for the 4-bit formats
+//    with 16-row blocks straight from memory, one slot per K step) and read
+//    back in the MFMA operand layout;
 //  * codes are decoded in registers and fed to v_mfma_f32_16x16x32_bf16
 //    (v_mfma_f32_16x16x32_fp8_fp8 for the static path) with fp32
 //    accumulation.  Lane (g, c) with g = lane/16, c = lane%16 supplies
@@ -82,14 +83,25 @@ struct XStage {
   }
 };
 
-// LDS: [activation slots of the NW waves (XLDS)][NW wave partials, fp32]
-template <int F, int MT, int NTW, int NW>
-constexpr int xslots_bytes(bool xlds) {
-  return xlds ? NW * XStage<F, MT>::SLOT : 0;
+// XDMA: the activation slices go from memory straight into LDS (buffer_load
+// ... lds), one slot per K step of the wave, instead of through registers and
+// a write into one slot (16-row blocks of 32-column tiles in tile order).
+// Measured at N = 4096, K = 3072, M = 32 (two alternating bench runs):
+// MXFP4 5.39 -> 5.24-5.26 us, INT4 6.01-6.02 -> 5.99-6.00 us; FP8 did not
+// change (6.16-6.18 against 6.16 us) and keeps the register staging
+template <int F, int MT, int NTW, int WL>
+constexpr bool x_dma() {
+  return MT == 1 && NTW == 2 && WL == kLayoutTiles && (F == KF_INT4 || F == KF_INT4A || F == KF_MXFP4);
 }
-template <int F, int MT, int NTW, int NW>
+
+// LDS: [activation slots of the NW waves (XLDS)][NW wave partials, fp32]
+template <int F, int MT, int NTW, int NW, int WL, int SPW>
+constexpr int xslots_bytes(bool xlds) {
+  return xlds ? NW * XStage<F, MT>::SLOT * (x_dma<F, MT, NTW, WL>() ? SPW : 1) : 0;
+}
+template <int F, int MT, int NTW, int NW, int WL, int SPW>
 constexpr int smem_bytes(bool xlds) {
-  return xslots_bytes<F, MT, NTW, NW>(xlds) + NW * (MT * 16 * 16 * NTW) * 4;
+  return xslots_bytes<F, MT, NTW, NW, WL, SPW>(xlds) + NW * (MT * 16 * 16 * NTW) * 4;
 }
 
 // Weights before activations (no-split tiles): every wave issues its packed
@@ -130,7 +142,8 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
   using XS = XStage<F, MT>;
   static_assert(!XLDS || XS::R * MT * XL == 16 * MT, "XLDS: load instructions must cover the slice rows");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* red = reinterpret_cast<float*>(smem + xslots_bytes<F, MT, NTW, NW>(XLDS));
+  float* red = reinterpret_cast<float*>(smem + xslots_bytes<F, MT, NTW, NW, WL, SPW>(XLDS));
+  constexpr bool XDMA = XLDS && x_dma<F, MT, NTW, WL>();
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -198,6 +211,8 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     u32x4 xv[SPW][MT][XL];
     uint32_t sc[SPW][NTW];
     auto load_x = [&]() {
+      // XDMA: the slots' reads of the previous pass are done before they refill
+      if constexpr (XDMA) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 #pragma unroll
       for (int st = 0; st < SPW; ++st) {
         const int kl = (blk * SPW + st) * MACRO + g * KPL;
@@ -207,7 +222,19 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
           const uint32_t m = (uint32_t)(m0 + 16 * i + c);
 #pragma unroll
           for (int j = 0; j < XL; ++j) {
-            if constexpr (XLDS) {
+            if constexpr (XDMA) {
+              // instruction q fills rows q*R .. q*R+R-1 of step st's slot:
+              // lane L writes position L % L_ of its row, so it loads the
+              // chunk the slot map puts there (the map is its own inverse)
+              const int q = i * XL + j;
+              const int rr = q * XS::R + lane / XS::L;
+              const uint32_t row = (uint32_t)(m0 + rr);
+              const int kx = (blk * SPW + st) * MACRO + XS::pos(rr, lane % XS::L) * (16 / XS::XB);
+              unsigned char* dst = smem + (wave * SPW + st) * XS::SLOT + q * 1024;
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                  Xr, (__attribute__((address_space(3))) void*)dst, 16,
+                  off_if(kx < K, (row * (uint32_t)K + (uint32_t)kx) * (uint32_t)XS::XB), 0, 0, 0);
+            } else if constexpr (XLDS) {
               // contiguous: instruction q covers rows q*R .. q*R+R-1 of the slice
               const int q = i * XL + j;
               const uint32_t row = (uint32_t)(m0 + q * XS::R + lane / XS::L);
@@ -301,19 +328,24 @@ __global__ __launch_bounds__(NW * 64) void k_linear(LinearArgs a, int S) {
     }
 
     // ---- decode and multiply
+    // XDMA: every activation load of the block has landed in LDS (they were
+    // issued after the weights, whose registers the decode has waited for)
+    if constexpr (XDMA) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
     for (int st = 0; st < SPW; ++st) {
       if constexpr (XLDS) {
         // through this wave's LDS slot into the operand layout (a wave's LDS
         // operations execute in order, so no barrier is needed here)
-        unsigned char* slot = smem + wave * XS::SLOT;
+        unsigned char* slot = smem + (wave * (XDMA ? SPW : 1) + (XDMA ? st : 0)) * XS::SLOT;
+        if constexpr (!XDMA) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+          for (int i = 0; i < MT; ++i)
 #pragma unroll
-          for (int j = 0; j < XL; ++j) {
-            const int row = (i * XL + j) * XS::R + lane / XS::L;
-            *reinterpret_cast<u32x4*>(slot + row * XS::ROWB + XS::pos(row, lane % XS::L) * 16) = xv[st][i][j];
-          }
+            for (int j = 0; j < XL; ++j) {
+              const int row = (i * XL + j) * XS::R + lane / XS::L;
+              *reinterpret_cast<u32x4*>(slot + row * XS::ROWB + XS::pos(row, lane % XS::L) * 16) = xv[st][i][j];
+            }
+        }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -526,10 +558,11 @@ constexpr int spw_split() {
 template <int F, int MT, int NTW, int WL>
 hipError_t launch_nosplit(const LinearArgs& a, dim3 grid, hipStream_t s) {
   constexpr int NW = (NTW == 4) ? 8 : 12;
-  constexpr int sm = smem_bytes<F, MT, NTW, NW>(true);
+  constexpr int SPW = spw_nosplit<F>() * 12 / NW;
+  constexpr int sm = smem_bytes<F, MT, NTW, NW, WL, SPW>(true);
   static_assert(sm <= 160 * 1024, "no-split tile exceeds the LDS of a CU");
   static std::atomic<int> done{0};
-  auto k = k_linear<F, MT, NTW, NW, spw_nosplit<F>() * 12 / NW, true, WL>;
+  auto k = k_linear<F, MT, NTW, NW, SPW, true, WL>;
   hipError_t e = allow_smem(k, sm, done);
   if (e != hipSuccess) return e;
   k<<<grid, NW * 64, sm, s>>>(a, 1);
@@ -540,7 +573,7 @@ template <int F, int MT, int WL>
 hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   dim3 grid(p.gx, p.S, p.gz);
   if (p.cfg == kCfgSplit) {
-    constexpr int sm = smem_bytes<F, MT, 4, 4>(false);
+    constexpr int sm = smem_bytes<F, MT, 4, 4, WL, spw_split<F>()>(false);
     k_linear<F, MT, 4, 4, spw_split<F>(), false, WL><<<grid, 256, sm, s>>>(a, p.S);
     if (p.S > 1) k_splitk_reduce<F, MT, 4, 4><<<dim3(p.gx, 1, p.gz), 256, 0, s>>>(a, p.S);
   } else {
@@ -553,7 +586,7 @@ hipError_t launch_mt(const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
         // 12 waves staged 5.2 us, direct 5.0 us, 6 waves direct 4.5 us; with
         // cold weights both direct forms take 4.8 us; from four rows up the
         // 12 staged waves win)
-        constexpr int sm = smem_bytes<F, MT, 1, 6>(false);
+        constexpr int sm = smem_bytes<F, MT, 1, 6, WL, 2 * spw_nosplit<F>()>(false);
         k_linear<F, MT, 1, 6, 2 * spw_nosplit<F>(), false, WL><<<grid, 384, sm, s>>>(a, p.S);
         return hipGetLastError();
       }
