@@ -340,7 +340,11 @@ wq_status wq_fp8_static_mlp2(const void* X, int64_t M, int64_t K1, const float* 
  * E2M1 x E2M1 scaled matrix cores (fp32 accumulation).  Wq/Ws: the packed
  * weight and E8M0 scales of wq_quantize + wq_pack for WQ_MXFP4, in `layout`
  * (the activations Xq/Xs are always row-major).  N % 32 == 0, K % 32 == 0.
- * No workspace.
+ * No workspace.  With K % 128 == 0 and 4-byte aligned Xs and Ws the kernels
+ * load the block scales as dwords (and from 9 rows with K % 512 == 0 copy the
+ * activation rows into LDS); other shapes and alignments take byte loads.  Up
+ * to 64 rows both forms give the same bits; above, the kernel (and with it
+ * the fp32 summation order) can differ between them.
  *
  * wq_mxfp4_dynamic_linear: wq_mx_quantize_act into the workspace, then
  * wq_mx_linear.  Workspace: wq_mxfp4_dynamic_workspace(M, K) bytes.
