@@ -36,6 +36,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -260,6 +261,14 @@ def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
     return res
 
 
+def sqnr_db(ref, y):
+    """10 log10(sum ref^2 / sum (ref - y)^2) of two bf16 device tensors, in fp64."""
+    r = ref.double().cpu()
+    e = r - y.double().cpu()
+    den = float((e * e).sum())
+    return round(10.0 * math.log10(float((r * r).sum()) / den), 2) if den > 0 else float("inf")
+
+
 def mlp2_timing(dev, capture, reps):
     """The static page's model (32 x 256 -> 512 -> 128, no bias) as one fused
     kernel and as two unfused static layers (four launches); weights warm."""
@@ -289,6 +298,13 @@ def mlp2_timing(dev, capture, reps):
             wq.wq_fp8_static_linear(H, s2, q2["codes"], q2["scales"], None, Y, ws)
 
     out = {}
+    # accuracy of the quantized model against the same model in bf16 (the
+    # page reports SQNR in dB): the fused kernel's output against two dense
+    # bf16 Linears (bf16 hidden layer), on the same input
+    fused(0, 1)
+    Yf = wq.linear(wq.linear(X, wq.dense(W1)), wq.dense(W2))
+    torch.cuda.synchronize()
+    out["static_mlp2_sqnr_db_vs_bf16"] = sqnr_db(Yf, Y)
     for name, fn, launches in (("static_mlp2_fused_M32", fused, 1), ("static_mlp2_unfused_M32", unfused, 4)):
         g = capture(fn, reps)
         g.replay()
@@ -334,7 +350,7 @@ def main_bench(args):
         for _ in range(copies - 1):
             rows.append({"packed": q0["packed"].clone(), "scales": q0["scales"].clone(),
                          "global": None if q0["global"] is None else q0["global"].clone()})
-        lay = {"reps": reps, "rows": rows, "X": synth.as_torch_bf16(X, dev),
+        lay = {"reps": reps, "rows": rows, "X": synth.as_torch_bf16(X, dev), "W": synth.as_torch_bf16(W, dev),
                "bias": synth.as_torch_bf16(b, dev) if b is not None else None,
                "Y": torch.empty((M, N), dtype=torch.bfloat16, device=dev), "fmt": qfmt}
         if fmt == "static_fp8":
@@ -475,6 +491,17 @@ def main_bench(args):
 
     sweep = None if args.no_sweep else m_sweep(layers, dev, capture)
 
+    # accuracy against the unquantized layer: each step kernel's M=32 output
+    # against the same layer in bf16 (dense bf16 weight, the library's bf16
+    # Linear), outside the timed region
+    sqnr = {}
+    for name in STEP:
+        lay = layers[name]
+        launch(name, 0, hot=True)
+        ref = wq.linear(lay["X"], wq.dense(lay["W"]), lay["bias"])
+        torch.cuda.synchronize()
+        sqnr[name] = sqnr_db(ref, lay["Y"])
+
     out = {
         "metric": METRIC,
         "value": round(value, 4),
@@ -495,6 +522,7 @@ def main_bench(args):
         "roofline": roofline,
         "per_format": per_format,
         "per_kernel": per_kernel,
+        "sqnr_db_vs_bf16": sqnr,
         "kernel_source_sha256": kernel_source_hash(),
         "wall_s_timed": round(t_wall, 4),
     }
