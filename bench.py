@@ -238,6 +238,12 @@ def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
                         wq.wq_linear("mxfp4", X, r["packed"], r["scales"], None, lay["bias"], N, Y, ws, LAYOUT)
 
             reps = reps_small if Mv <= 256 else reps_large
+            # accuracy against the same layer in bf16 (outside the timed replays)
+            run(0, 1)
+            ref = wq.linear(X, wq.dense(lay["W"]), None if fmt == "static_fp8" else lay["bias"])
+            torch.cuda.synchronize()
+            sq = sqnr_db(ref, Y)
+            del ref
             g = capture(run, reps)
             g.replay()
             torch.cuda.synchronize()
@@ -255,6 +261,7 @@ def m_sweep(layers, dev, capture, reps_small=200, reps_large=30):
                 "pct_mfma_peak": round(100.0 * flop / (us * 1e-6) / 1e12 / peak[fmt], 2),
                 "effective_TBps": round(eff / (us * 1e-6) / 1e12, 4),
                 "launches": 1 if fmt == "mxfp4" else 2,
+                "sqnr_db_vs_bf16": sq,
             }
             del g
     res.update(mlp2_timing(dev, capture, reps_small))
