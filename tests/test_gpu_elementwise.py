@@ -6,8 +6,8 @@ checks the outputs as a whole; this checks each one, at the benchmark's full
 size and in the other launch configurations: one and two rows (operand
 loads straight from memory), 32 rows (the benchmark's 16-row blocks, both
 layouts), 100 rows on a wide layer (64-column tiles), 256 rows (the mid-M
-kernel), a split-K narrow layer, and sampled rows at M = 4096 (256 x 256
-tiles).  The worst ratio |y - ref| / bound is printed per case."""
+kernel), 24 rows over a long K (two passes of the waves' K steps), a split-K
+narrow layer, and sampled rows at M = 4096 (256 x 256 tiles).  The worst ratio |y - ref| / bound is printed per case."""
 
 import numpy as np
 import pytest
@@ -56,6 +56,12 @@ def test_elementwise_m32_rows_layout(fmt):
 @pytest.mark.parametrize("M", [1, 2, 100, 256])
 def test_elementwise_other_row_counts(fmt, M):
     _check(fmt, M, 4096, 3072, cfg=400 + M)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_elementwise_m24_long_k(fmt):
+    # 16-row blocks in tile order, the waves' K steps in two passes
+    _check(fmt, 24, 4096, 6144, cfg=415)
 
 
 @pytest.mark.parametrize("fmt", FMTS)

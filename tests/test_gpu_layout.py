@@ -69,6 +69,7 @@ def _layer(fmt, N, K, M, cfg, bias=True):
 LINEAR_CASES = [
     (1, 4096, 3072), (2, 1024, 1024),          # one/two rows
     (16, 4096, 3072), (32, 4096, 3072),        # 16/32-row no-split (headline)
+    (24, 4096, 6144), (32, 4096, 8192),        # the same over two and three passes of the waves' K steps
     (48, 4096, 3072), (64, 1024, 2048),        # two row blocks, 32- / 16-column tiles
     (100, 4096, 3072),                         # 65-128 rows: 64-column tiles
     (32, 256, 4096), (7, 512, 8192),           # split K + reduction
