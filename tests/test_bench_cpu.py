@@ -1,7 +1,8 @@
 """Host logic of bench.py (no GPU): byte accounting of the metric and the
-roofline, the source-hash gate on the committed counter profile, and the
-one-GPU guard."""
+roofline, the source-hash gate on the committed counter profile, the SQNR
+helper and the one-GPU guard."""
 import json
+import math
 import os
 import subprocess
 import sys
@@ -74,3 +75,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_sqnr_db_closed_forms():
+    """The SQNR the bench reports: a uniform relative error e gives -20 log10(e)
+    dB; identical outputs give infinity; bf16 inputs are widened exactly."""
+    import torch
+
+    ref = torch.full((4, 8), 3.0, dtype=torch.bfloat16)
+    y = ref * (1 + 2.0 ** -6)  # 3 * (1 + 1/64) is exact in bf16
+    assert bench.sqnr_db(ref, y) == pytest.approx(-20 * math.log10(2.0 ** -6), abs=0.01)
+    assert bench.sqnr_db(ref, ref.clone()) == float("inf")
+    # a sign flip of half the elements: error power 4x half the signal -> -3.01 dB
+    z = ref.clone()
+    z[:2] = -z[:2]
+    assert bench.sqnr_db(ref, z) == pytest.approx(-10 * math.log10(2.0), abs=0.01)
